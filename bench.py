@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Throughput of the HQQ quantizer on one MI355X.
+
+A step quantizes one whole Llama-2-7B-shaped stack (32 blocks x q,k,v,o,gate,up,down,
+224 tensors, 6.48e9 binary16 weights resident in HBM; 4-bit, group 64... see --workload)
+through the C ABI: the group solver over every tensor, then the per-tensor 8-bit zero
+requantization. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+METRIC = "fp16 weight GB/s quantized (% HBM peak); seconds per Llama-2-7B-shaped stack"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(spec) -> float:
+    """Algorithmic HBM bytes of one tensor: read binary16 weights once, write packed codes,
+    binary16 scale and the zero (2 bytes, or 1 for 8-bit zeros) once per group."""
+    from calibration_free_weight_amd import hqq
+    n = spec.numel
+    ng = n // spec.group_size
+    zb = 2 if spec.zero_bits == 16 else 1
+    return 2.0 * n + hqq.hqq_packed_bytes(n, spec.nbits) + ng * (2 + zb)
+
+
+def cpu_baseline(specs, weights, seconds):
+    """The oracle, single-threaded, on a bounded sample of the same weights: leading rows of
+    each distinct projection of block 0, grown until about `seconds` of CPU work."""
+    import numpy as np
+    import oracle
+    from synth import half_bits
+    O = oracle.Oracle()
+    block0 = [(s, w) for s, w in zip(specs, weights) if s.block == 0]
+    # calibrate on a small slice, then size the sample
+    s0, w0 = block0[0]
+    probe_rows = max(1, 65536 // s0.cols)
+    x = half_bits(w0[:probe_rows]).reshape(-1)
+    t = time.perf_counter()
+    O.solve_groups(x, s0.group_size, s0.nbits)
+    rate = x.size / (time.perf_counter() - t)
+    per_tensor = rate * seconds / len(block0)
+    total_w, total_t, parts = 0, 0.0, []
+    for s, w in block0:
+        rows = int(max(1, min(s.rows, per_tensor // s.cols)))
+        x = half_bits(w[:rows]).reshape(-1)
+        t = time.perf_counter()
+        O.quantize(x, s.group_size, s.nbits, zero_bits=s.zero_bits)
+        total_t += time.perf_counter() - t
+        total_w += x.size
+        parts.append(f"{s.name}[:{rows}]")
+    return dict(value=round(2.0 * total_w / total_t / 1e9, 6), unit="GB/s", cores=1,
+                kind="oracle",
+                sample=f"{total_w} weights ({', '.join(parts)}), one thread, "
+                       f"{total_t:.1f} s; full quantize incl. zero storage and packing")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the quantizer shards by whole tensors with no communication)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from calibration_free_weight_amd import hqq
+
+    dev = torch.device("cuda:0")
+    specs = synth.workload(args.workload)
+    n_weights = sum(s.numel for s in specs)
+    log(f"bench: workload {args.workload} ({synth.WORKLOAD_NAMES[args.workload]}), "
+        f"{len(specs)} tensors, {n_weights / 1e9:.3f}e9 weights")
+    # Inputs resident in HBM; outputs and workspace preallocated.
+    weights, outs, jobs = [], [], []
+    for s in specs:
+        w = synth.student_t_weights(s.rows, s.cols, s.seed(args.workload), device=dev)
+        o = hqq.alloc_outputs(s.rows, s.cols, s.nbits, s.group_size, s.zero_bits, dev)
+        jobs.append(hqq.make_job(w, s.nbits, s.group_size, 1, 0.7, 1.0, 1.01, 20, 1,
+                                 s.zero_bits, o["packed"], o["scale"], o["zero"],
+                                 o["zero_meta"]))
+        weights.append(w)
+        outs.append(o)
+    ws = hqq.alloc_workspace(jobs, dev)
+    # Config 1 fits the 256 MB last-level cache: rotate 16 input/output sets so every step
+    # streams from HBM.
+    job_sets = [jobs]
+    keep = []
+    if args.workload == 1:
+        for r in range(15):
+            s = specs[0]
+            w = synth.student_t_weights(s.rows, s.cols, s.seed(1) + 7919 * (r + 1), device=dev)
+            o = hqq.alloc_outputs(s.rows, s.cols, s.nbits, s.group_size, s.zero_bits, dev)
+            keep.append((w, o))
+            job_sets.append([hqq.make_job(w, s.nbits, s.group_size, 1, 0.7, 1.0, 1.01, 20, 1,
+                                          s.zero_bits, o["packed"], o["scale"], o["zero"],
+                                          o["zero_meta"])])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    log("bench: inputs ready")
+
+    for i in range(args.warmup):
+        hqq.hqq_quantize_batch(job_sets[i % len(job_sets)], ws, stream.cuda_stream)
+    torch.cuda.synchronize()
+    log("bench: warmup done")
+
+    # Events on the stream the kernels run on: the solver phase of each step is bracketed.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        js = job_sets[k % len(job_sets)]
+        ev[k][0].record(stream)
+        hqq.hqq_solve_batch(js, ws, stream.cuda_stream)
+        ev[k][1].record(stream)
+        hqq.hqq_requant_batch(js, ws, stream.cuda_stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    log("bench: timed steps done")
+
+    sec_per_step = (t1 - t0) / args.steps
+    value = 2.0 * n_weights / sec_per_step / 1e9
+    solve_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    launches = len(specs)                    # one solver launch per tensor
+    bytes_step = sum(alg_bytes(s) for s in specs)
+    achieved = bytes_step / (solve_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": synth.WORKLOAD_NAMES[args.workload], "tensors": len(specs),
+                   "weights": n_weights, "p": 0.7, "beta": 1.0, "kappa": 1.01, "iters": 20,
+                   "early_stop": True},
+        "seconds_per_stack": round(sec_per_step, 6),
+        "pct_hbm_peak": round(100.0 * bytes_step / sec_per_step / 1e9 / HBM_PEAK_GBS, 3),
+        "roofline": {"bound": "hbm", "kernel": "solve_kernel",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_ms": round(solve_ms / launches, 5),
+                     "bytes_per_launch": round(bytes_step / launches, 1)},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(specs, weights, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

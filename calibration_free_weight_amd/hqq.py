@@ -1,0 +1,199 @@
+"""Python binding of libhqq: the C ABI of include/hqq.h, argument marshalling only.
+
+Every compute step runs in the HIP library; this module passes device pointers
+(``tensor.data_ptr()``), sizes and the current HIP stream through ctypes. PyTorch provides
+device memory and streams. There is no fallback: if the library is missing the import of a
+function raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhqq.so")
+
+HQQ_OK, HQQ_ERR_ARG, HQQ_ERR_UNSUPPORTED, HQQ_ERR_WORKSPACE, HQQ_ERR_DEVICE = range(5)
+
+# Functions declared in include/hqq.h (checked by the tests against the header).
+EXPORTS = ("hqq_packed_bytes", "hqq_workspace_bytes", "hqq_quantize", "hqq_quantize_batch",
+           "hqq_solve_batch", "hqq_requant_batch", "hqq_dequantize", "hqq_pack", "hqq_unpack",
+           "hqq_status_string", "hqq_last_error")
+
+
+class HQQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class hqq_job(C.Structure):
+    _fields_ = [("W", C.c_void_p), ("rows", C.c_int64), ("cols", C.c_int64),
+                ("nbits", C.c_int), ("group_size", C.c_int), ("axis", C.c_int),
+                ("p", C.c_float), ("beta", C.c_float), ("kappa", C.c_float),
+                ("iters", C.c_int), ("early_stop", C.c_int), ("zero_bits", C.c_int),
+                ("packed", C.c_void_p), ("scale", C.c_void_p), ("zero", C.c_void_p),
+                ("zero_meta", C.c_void_p), ("passes", C.c_void_p)]
+
+
+_L = None
+
+
+def lib():
+    """The loaded library. Raises if it has not been built (no CPU fallback exists)."""
+    global _L
+    if _L is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        vp, i64, i32, f32 = C.c_void_p, C.c_int64, C.c_int, C.c_float
+        L.hqq_packed_bytes.restype = C.c_size_t
+        L.hqq_packed_bytes.argtypes = [i64, i32]
+        L.hqq_workspace_bytes.restype = C.c_size_t
+        L.hqq_workspace_bytes.argtypes = [C.POINTER(hqq_job), i32]
+        L.hqq_quantize.restype = i32
+        L.hqq_quantize.argtypes = [vp, i64, i64, i32, i32, i32, f32, f32, f32, i32, i32, i32,
+                                   vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        for name in ("hqq_quantize_batch", "hqq_solve_batch", "hqq_requant_batch"):
+            getattr(L, name).restype = i32
+            getattr(L, name).argtypes = [C.POINTER(hqq_job), i32, vp, C.c_size_t, vp]
+        L.hqq_dequantize.restype = i32
+        L.hqq_dequantize.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp]
+        L.hqq_pack.restype = i32
+        L.hqq_pack.argtypes = [vp, i64, i32, vp, vp]
+        L.hqq_unpack.restype = i32
+        L.hqq_unpack.argtypes = [vp, i64, i32, vp, vp]
+        L.hqq_status_string.restype = C.c_char_p
+        L.hqq_status_string.argtypes = [i32]
+        L.hqq_last_error.restype = C.c_char_p
+        L.hqq_last_error.argtypes = []
+        _L = L
+    return _L
+
+
+def _p(t):
+    """Device pointer of a tensor (or None)."""
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return C.c_void_p(int(stream))
+    import torch
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(st: int):
+    if st != HQQ_OK:
+        L = lib()
+        raise HQQError(st, f"{L.hqq_status_string(st).decode()}: {L.hqq_last_error().decode()}")
+
+
+def hqq_status_string(status: int) -> str:
+    return lib().hqq_status_string(status).decode()
+
+
+def hqq_last_error() -> str:
+    return lib().hqq_last_error().decode()
+
+
+def hqq_packed_bytes(n_codes: int, nbits: int) -> int:
+    return int(lib().hqq_packed_bytes(n_codes, nbits))
+
+
+def make_job(W, nbits, group_size, axis, p, beta, kappa, iters, early_stop, zero_bits,
+             packed, scale, zero, zero_meta, passes=None) -> hqq_job:
+    rows, cols = W.shape
+    return hqq_job(_p(W), rows, cols, nbits, group_size, axis, p, beta, kappa, iters,
+                   int(early_stop), zero_bits, _p(packed), _p(scale), _p(zero),
+                   _p(zero_meta), _p(passes))
+
+
+def hqq_workspace_bytes(jobs) -> int:
+    arr = (hqq_job * len(jobs))(*jobs)
+    n = int(lib().hqq_workspace_bytes(arr, len(jobs)))
+    if n == (1 << 64) - 1:
+        raise HQQError(HQQ_ERR_ARG, "invalid job in workspace query")
+    return n
+
+
+def hqq_quantize(W, nbits, group_size, axis, p, beta, kappa, iters, early_stop, zero_bits,
+                 packed, scale, zero, zero_meta, passes, workspace, stream=None) -> None:
+    rows, cols = W.shape
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hqq_quantize(_p(W), rows, cols, nbits, group_size, axis, p, beta, kappa,
+                              iters, int(early_stop), zero_bits, _p(packed), _p(scale),
+                              _p(zero), _p(zero_meta), _p(passes), _p(workspace), wsb,
+                              _stream(stream)))
+
+
+def _batch(fn, jobs, workspace, stream):
+    arr = (hqq_job * len(jobs))(*jobs)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn(arr, len(jobs), _p(workspace), wsb, _stream(stream)))
+
+
+def hqq_quantize_batch(jobs, workspace, stream=None) -> None:
+    _batch(lib().hqq_quantize_batch, jobs, workspace, stream)
+
+
+def hqq_solve_batch(jobs, workspace, stream=None) -> None:
+    _batch(lib().hqq_solve_batch, jobs, workspace, stream)
+
+
+def hqq_requant_batch(jobs, workspace, stream=None) -> None:
+    _batch(lib().hqq_requant_batch, jobs, workspace, stream)
+
+
+def hqq_dequantize(packed, scale, zero, zero_meta, rows, cols, nbits, group_size, axis,
+                   zero_bits, W_out, stream=None) -> None:
+    _check(lib().hqq_dequantize(_p(packed), _p(scale), _p(zero), _p(zero_meta), rows, cols,
+                                nbits, group_size, axis, zero_bits, _p(W_out),
+                                _stream(stream)))
+
+
+def hqq_pack(codes, n_codes, nbits, packed, stream=None) -> None:
+    _check(lib().hqq_pack(_p(codes), n_codes, nbits, _p(packed), _stream(stream)))
+
+
+def hqq_unpack(packed, n_codes, nbits, codes, stream=None) -> None:
+    _check(lib().hqq_unpack(_p(packed), n_codes, nbits, _p(codes), _stream(stream)))
+
+
+# ---- allocation helpers (PyTorch device memory for the outputs) -----------------------------
+def alloc_outputs(rows, cols, nbits, group_size, zero_bits, device, passes=False):
+    """Output tensors of one job: packed (uint8, 16-byte aligned by the allocator), scale,
+    zero, zero_meta (or None) and passes (or None)."""
+    import torch
+    ng = rows * cols // group_size
+    out = dict(
+        packed=torch.empty(max(hqq_packed_bytes(rows * cols, nbits), 1), dtype=torch.uint8,
+                           device=device),
+        scale=torch.empty(ng, dtype=torch.float16, device=device),
+        zero=torch.empty(ng, dtype=torch.float16 if zero_bits == 16 else torch.uint8,
+                         device=device),
+        zero_meta=torch.empty(2, dtype=torch.float16, device=device) if zero_bits == 8 else None,
+        passes=torch.empty(ng, dtype=torch.uint8, device=device) if passes else None,
+    )
+    return out
+
+
+def alloc_workspace(jobs, device):
+    import torch
+    n = hqq_workspace_bytes(jobs)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def quantize(W, nbits, group_size, axis=1, p=0.7, beta=1.0, kappa=1.01, iters=20,
+             early_stop=True, zero_bits=16, passes=False, stream=None):
+    """Allocate outputs and a workspace, then call hqq_quantize. Returns the output dict."""
+    rows, cols = W.shape
+    out = alloc_outputs(rows, cols, nbits, group_size, zero_bits, W.device, passes)
+    job = make_job(W, nbits, group_size, axis, p, beta, kappa, iters, early_stop, zero_bits,
+                   out["packed"], out["scale"], out["zero"], out["zero_meta"], out["passes"])
+    ws = alloc_workspace([job], W.device)
+    hqq_quantize(W, nbits, group_size, axis, p, beta, kappa, iters, early_stop, zero_bits,
+                 out["packed"], out["scale"], out["zero"], out["zero_meta"], out["passes"],
+                 ws, stream)
+    out["workspace"] = ws
+    return out

@@ -1,0 +1,147 @@
+/*
+ * hqq.h -- C ABI of the MI355X (gfx950) HQQ weight quantizer.
+ *
+ * The method: Half-Quadratic Quantization, a calibration-free weight quantizer. Per group of
+ * `group_size` consecutive weights of a row it fixes the min-max scale, then optimises the
+ * zero-point by half-quadratic splitting of an lp (p < 1) reconstruction loss: a generalized
+ * soft-threshold of the residual alternates with a closed-form average for the zero, with
+ * beta growing by kappa each iteration, for about 20 iterations with early stopping.
+ * Sources:
+ *   [TR] techreport.ngo, "Half-Quadratic Quantization of Large Machine Learning Models",
+ *        sections "Outlier-aware optimization without gradients" (the solver) and
+ *        "Benchmark results / Llama-2" (p = 0.7, beta = 1, kappa = 1.01, 20 iterations with
+ *        early stopping; zero-point quantized to 8 bit without grouping or optimisation).
+ *   [SK] "HQQ - Half-Quadratic Quantization" usage guide, sections "Core concepts /
+ *        Quantization configuration" (nbits, group_size, axis) and "HQQLinear layer"
+ *        (W_q, scale, zero, dequantize()).
+ *
+ * Conventions common to every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller. The library allocates no
+ *    memory and keeps no state between calls; scratch space is the caller's `workspace`.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue work on it and
+ *    never synchronise; a device fault surfaces at the caller's next synchronisation.
+ *  - Arguments are validated on the host before any HIP call. A rejected call returns a
+ *    non-zero hqq_status, enqueues nothing and leaves a message in hqq_last_error().
+ *  - Inputs must be finite; results for NaN/Inf weights are unspecified.
+ *  - Calls are reentrant; concurrent calls need distinct workspaces and outputs.
+ *  - Layouts: W is binary16, row-major [rows, cols], contiguous. With axis = 1 a group is
+ *    `group_size` consecutive elements of a row, so the tensor is a flat array of
+ *    n_groups = rows*cols/group_size contiguous groups, numbered in memory order.
+ *  - Packed codes: one flat stream in memory order; code k of a container occupies bits
+ *    [nbits*k, nbits*k + nbits). 8/4/2/1-bit codes fill uint8 containers (1/2/4/8 per byte);
+ *    3-bit codes fill little-endian uint32 containers, 10 per word, bits 30-31 zero.
+ *    Unused trailing bits are zero. Size: hqq_packed_bytes(rows*cols, nbits).
+ *  - Reconstruction: W_r = (q - zero) * scale, where `scale` stores 1/s for the solver's
+ *    quantizer multiplier s and `zero` the solver's zero-point (binary16), or for 8-bit
+ *    zeros zero = zq * zero_meta[0] + zero_meta[1] with one binary16 pair per tensor.
+ */
+#ifndef HQQ_H
+#define HQQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hqq_status {
+    HQQ_OK = 0,
+    HQQ_ERR_ARG = 1,         /* invalid argument (null, misaligned, out of range)       */
+    HQQ_ERR_UNSUPPORTED = 2, /* valid for the method but not built here (e.g. axis = 0)  */
+    HQQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than hqq_workspace_bytes()  */
+    HQQ_ERR_DEVICE = 4       /* a HIP call failed; see hqq_last_error()                  */
+} hqq_status;
+
+/* One tensor and its quantizer parameters (the single-tensor call is a batch of one).
+ * Field meanings are those of hqq_quantize below. */
+typedef struct hqq_job {
+    const void *W;           /* binary16 [rows, cols], 16-byte aligned                     */
+    int64_t rows, cols;
+    int nbits;               /* 1, 2, 3, 4 or 8 [SK "Quantization configuration"]          */
+    int group_size;          /* 16, 32, 64, 128 or 256; divides cols                       */
+    int axis;                /* 1 (groups along rows); 0 -> HQQ_ERR_UNSUPPORTED            */
+    float p, beta, kappa;    /* lp exponent (0 < p <= 1), initial beta, beta growth [TR]   */
+    int iters;               /* 0..254 half-quadratic iterations; 0 = min-max RTN          */
+    int early_stop;          /* 1: stop a group when its error rises; 0: run all iters     */
+    int zero_bits;           /* 16: binary16 zeros; 8: uint8 zeros + per-tensor meta [TR]  */
+    void *packed;            /* out: hqq_packed_bytes(rows*cols, nbits) bytes, 16-B aligned */
+    void *scale;             /* out: binary16 [n_groups]                                    */
+    void *zero;              /* out: binary16 [n_groups] or uint8 [n_groups]                */
+    void *zero_meta;         /* out: binary16 [2] when zero_bits == 8, else NULL            */
+    uint8_t *passes;         /* out, nullable: evaluations run per group (instrumentation)  */
+} hqq_job;
+
+/* Bytes of the packed code stream for n_codes codes of nbits bits (0 for invalid nbits):
+ * ceil(n*nbits/8) for 8/4/2/1 bits, 4*ceil(n/10) for 3 bits. */
+size_t hqq_packed_bytes(int64_t n_codes, int nbits);
+
+/* Workspace bytes hqq_quantize_batch needs for these jobs (host array). The workspace holds
+ * the device copy of the job table, binary32 zero staging for 8-bit zero requantization and
+ * the per-tensor reductions (0 when every job stores binary16 zeros). Returns SIZE_MAX if
+ * a job is invalid; the quantize call then reports why. */
+size_t hqq_workspace_bytes(const hqq_job *jobs, int n_jobs);
+
+/* Quantize one tensor [TR "Outlier-aware optimization without gradients"].
+ * Per group: s = qmax/(max - min), z0 = -min*s (binary32), then up to `iters` iterations of
+ *   W_e = sign(r)*max(|r| - |r|^(p-1)/beta, 0), r = W - (q - z)/s  (generalized soft-threshold)
+ *   z   = mean(q - (W - W_e)*s)                                      (closed-form zero update)
+ *   beta = beta*kappa, q = clamp(round(W*s + z), 0, 2^nbits - 1)
+ * keeping the iterate with the lowest mean |W - (q - z)/s| and stopping when it rises
+ * (early_stop). Per-element arithmetic is exact; the zero is rounded to binary32 at each
+ * update. Outputs: packed codes, scale = binary16(1/s), zero (see hqq_job), passes.
+ * workspace: device buffer (256-byte aligned) of at least hqq_workspace_bytes() for this one
+ * job; 0 bytes are needed for zero_bits == 16 and workspace may then be NULL. With
+ * zero_bits == 8 its first 4*n_groups bytes hold, after the call, the binary32 zeros the
+ * solver returned (before 8-bit requantization). */
+hqq_status hqq_quantize(const void *W, int64_t rows, int64_t cols, int nbits, int group_size,
+                        int axis, float p, float beta, float kappa, int iters, int early_stop,
+                        int zero_bits, void *packed, void *scale, void *zero, void *zero_meta,
+                        uint8_t *passes, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Quantize several tensors with one launch sequence (e.g. every linear layer of a model
+ * stack). `jobs` is a host array, read during the call only; every job is validated first.
+ * Jobs may mix nbits and group sizes; each job's output is what hqq_quantize writes. */
+hqq_status hqq_quantize_batch(const hqq_job *jobs, int n_jobs, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* The two steps of hqq_quantize_batch, callable separately (e.g. to time them apart).
+ * hqq_solve_batch runs the group solver for every job: it writes packed codes, scale,
+ * passes and, for zero_bits == 16, the binary16 zeros; for zero_bits == 8 it leaves the
+ * binary32 zeros and their per-tensor reduction inputs in the workspace.
+ * hqq_requant_batch then quantizes those zeros to 8 bit [TR "Benchmark results / Llama-2"]
+ * and writes zero and zero_meta. It must be given the same jobs and workspace, after
+ * hqq_solve_batch on the same stream (it does nothing for zero_bits == 16 jobs). */
+hqq_status hqq_solve_batch(const hqq_job *jobs, int n_jobs, void *workspace,
+                           size_t workspace_bytes, void *stream);
+hqq_status hqq_requant_batch(const hqq_job *jobs, int n_jobs, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/* Reconstruct binary16 weights [SK "HQQLinear layer", dequantize()]:
+ * W_out = binary16((q - zero_f) * scale), zero_f the binary16 zero or, for zero_bits == 8,
+ * zq * zero_meta[0] + zero_meta[1] (one fused rounding). Same layouts as hqq_quantize. */
+hqq_status hqq_dequantize(const void *packed, const void *scale, const void *zero,
+                          const void *zero_meta, int64_t rows, int64_t cols, int nbits,
+                          int group_size, int axis, int zero_bits, void *W_out, void *stream);
+
+/* Pack n_codes uint8 codes (each < 2^nbits) into the packed layout above; `packed` must be
+ * 16-byte aligned and hold hqq_packed_bytes(n_codes, nbits) bytes. Codes >= 2^nbits are
+ * masked to their low nbits bits. */
+hqq_status hqq_pack(const uint8_t *codes, int64_t n_codes, int nbits, void *packed,
+                    void *stream);
+
+/* Inverse of hqq_pack: n_codes uint8 codes out. */
+hqq_status hqq_unpack(const void *packed, int64_t n_codes, int nbits, uint8_t *codes,
+                      void *stream);
+
+/* Static text for a status code. */
+const char *hqq_status_string(hqq_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *hqq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HQQ_H */

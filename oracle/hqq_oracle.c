@@ -191,13 +191,14 @@ enum { HQO_MAX_G = 4096 };
  *
  * Outputs: codes[g], *s_out (quantizer multiplier s), *z_out (accepted zero), *passes
  * (number of evaluations, 1..iters+1), *last_change (last t at which the accepted zero
- * changed, 0 if never), *shrink_active (1 if any W_e was non-zero) and, when trace_S is not
+ * changed, 0 if never), *shrink_active (1 if any W_e was non-zero), *stopped (1 if the
+ * loop ended on a rise of the error) and, when trace_S is not
  * NULL, S of every evaluation in trace_S[0..passes-1] with trace_acc[k] = 1 when evaluation
  * k was accepted. Returns the accepted mean error S / (g*s). */
 double hqo_solve_group(const double *x, int g, int nbits, float p, float beta0, float kappa,
                        int iters, int early_stop, uint8_t *codes, float *s_out, float *z_out,
-                       int *passes, int *last_change, int *shrink_active, double *trace_S,
-                       uint8_t *trace_acc)
+                       int *passes, int *last_change, int *shrink_active, int *stopped,
+                       double *trace_S, uint8_t *trace_acc)
 {
     assert(g >= 1 && g <= HQO_MAX_G);
     for (int j = 0; j < g; ++j) assert(isfinite(x[j]));
@@ -206,7 +207,7 @@ double hqo_solve_group(const double *x, int g, int nbits, float p, float beta0, 
     float s, z;
     hqo_init(x, g, qmax, &s, &z);
     double S_best = hqo_eval(x, g, s, z, qmax, q, r);
-    int np = 1, lc = 0, act = 0;
+    int np = 1, lc = 0, act = 0, rose = 0;
     if (trace_S) { trace_S[0] = S_best; trace_acc[0] = 1; }
     float beta = beta0;
     for (int t = 1; t <= iters; ++t) {
@@ -219,7 +220,10 @@ double hqo_solve_group(const double *x, int g, int nbits, float p, float beta0, 
         double S_new = hqo_eval(x, g, s, z_new, qmax, qn, rn);
         if (trace_S) { trace_S[np] = S_new; trace_acc[np] = 0; }
         np += 1;
-        if (early_stop && S_new > S_best) break;
+        if (early_stop && S_new > S_best) {
+            rose = 1;
+            break;
+        }
         if (trace_S) trace_acc[np - 1] = 1;
         if (z_new != z) lc = t;
         z = z_new;
@@ -233,6 +237,7 @@ double hqo_solve_group(const double *x, int g, int nbits, float p, float beta0, 
     if (passes) *passes = np;
     if (last_change) *last_change = lc;
     if (shrink_active) *shrink_active = act;
+    if (stopped) *stopped = rose;
     return S_best / ((double)g * (double)s);
 }
 
@@ -246,22 +251,23 @@ double hqo_solve_group(const double *x, int g, int nbits, float p, float beta0, 
 void hqo_solve_groups(const uint16_t *w, int64_t n_groups, int g, int nbits, float p,
                       float beta, float kappa, int iters, int early_stop, uint8_t *codes,
                       uint16_t *scale, float *zero_f32, float *s_f32, uint8_t *passes,
-                      uint8_t *last_change, uint8_t *shrink_active)
+                      uint8_t *last_change, uint8_t *shrink_active, uint8_t *stopped)
 {
     double x[HQO_MAX_G];
     for (int64_t i = 0; i < n_groups; ++i) {
         const uint16_t *wg = w + i * (int64_t)g;
         for (int j = 0; j < g; ++j) x[j] = (double)hqo_half_to_float(wg[j]);
         float s, z;
-        int np, lc, act;
+        int np, lc, act, rose;
         hqo_solve_group(x, g, nbits, p, beta, kappa, iters, early_stop,
-                        codes + i * (int64_t)g, &s, &z, &np, &lc, &act, NULL, NULL);
+                        codes + i * (int64_t)g, &s, &z, &np, &lc, &act, &rose, NULL, NULL);
         scale[i] = hqo_float_to_half(1.0f / s);
         zero_f32[i] = z;
         if (s_f32) s_f32[i] = s;
         if (passes) passes[i] = (uint8_t)np;
         if (last_change) last_change[i] = (uint8_t)lc;
         if (shrink_active) shrink_active[i] = (uint8_t)act;
+        if (stopped) stopped[i] = (uint8_t)rose;
     }
 }
 
@@ -269,10 +275,12 @@ void hqo_solve_groups(const uint16_t *w, int64_t n_groups, int g, int nbits, flo
  * 16-bit: zero = binary16(z).
  * 8-bit [TR "Benchmark results / Llama-2": the zero-point goes to 8 bit with no extra
  * grouping and no optimisation]. Reading: one min-max affine uint8 round-to-nearest
- * quantizer over all zeros of the tensor; s_z = 255 / (zmax - zmin) (1 if all equal),
- * zq = clamp(round-half-even(z * s_z - zmin * s_z), 0, 255) with one fused rounding, and the
- * per-tensor meta pair {binary16(1/s_z), binary16(zmin)}, so that the stored zero reads back
- * as zq * meta[0] + meta[1]. */
+ * quantizer over all zeros of the tensor, on the grid its stored binary16 pair defines:
+ *   step = binary16((zmax - zmin) / 255)   (1 if that is 0: all zeros equal),
+ *   base = binary16(zmin),
+ *   zq   = clamp(round-half-even((z - base) / step), 0, 255)   (binary32 operations),
+ * meta = {step, base}; the stored zero reads back as zq * step + base. Quantizing against the
+ * stored pair (not the unrounded one) keeps the read-back within half a step. */
 void hqo_zero_requant(const float *z, int64_t n, uint8_t *zq, uint16_t *meta)
 {
     float zmin = z[0], zmax = z[0];
@@ -280,15 +288,21 @@ void hqo_zero_requant(const float *z, int64_t n, uint8_t *zq, uint16_t *meta)
         zmin = fminf(zmin, z[i]);
         zmax = fmaxf(zmax, z[i]);
     }
-    float sz = zmax > zmin ? 255.0f / (zmax - zmin) : 1.0f;
-    float c = -(zmin * sz);
+    uint16_t h_step = hqo_float_to_half((zmax - zmin) / 255.0f);
+    float step = hqo_half_to_float(h_step);
+    if (!(step > 0.0f)) {
+        h_step = 0x3c00;                            /* binary16 1.0 */
+        step = 1.0f;
+    }
+    uint16_t h_base = hqo_float_to_half(zmin);
+    float base = hqo_half_to_float(h_base);
     for (int64_t i = 0; i < n; ++i) {
-        float v = nearbyintf(fmaf(z[i], sz, c));
+        float v = nearbyintf((z[i] - base) / step);
         v = fminf(fmaxf(v, 0.0f), 255.0f);
         zq[i] = (uint8_t)v;
     }
-    meta[0] = hqo_float_to_half(1.0f / sz);
-    meta[1] = hqo_float_to_half(zmin);
+    meta[0] = h_step;
+    meta[1] = h_base;
 }
 
 void hqo_zero_to_half(const float *z, int64_t n, uint16_t *zh)

@@ -66,11 +66,12 @@ class Oracle:
         L.hqo_solve_group.argtypes = [_f64p, C.c_int, C.c_int, C.c_float, C.c_float, C.c_float,
                                       C.c_int, C.c_int, _u8p, C.POINTER(C.c_float),
                                       C.POINTER(C.c_float), C.POINTER(C.c_int),
-                                      C.POINTER(C.c_int), C.POINTER(C.c_int), _vp, _vp]
+                                      C.POINTER(C.c_int), C.POINTER(C.c_int),
+                                      C.POINTER(C.c_int), _vp, _vp]
         L.hqo_solve_groups.restype = None
         L.hqo_solve_groups.argtypes = [_u16p, C.c_int64, C.c_int, C.c_int, C.c_float, C.c_float,
                                        C.c_float, C.c_int, C.c_int, _u8p, _u16p, _f32p, _vp,
-                                       _vp, _vp, _vp]
+                                       _vp, _vp, _vp, _vp]
         L.hqo_zero_requant.restype = None
         L.hqo_zero_requant.argtypes = [_f32p, C.c_int64, _u8p, _u16p]
         L.hqo_zero_to_half.restype = None
@@ -129,14 +130,16 @@ class Oracle:
         np_ = C.c_int()
         lc = C.c_int()
         act = C.c_int()
+        rose = C.c_int()
         te = np.zeros(iters + 1, np.float64)
         ta = np.zeros(iters + 1, np.uint8)
         e = self.L.hqo_solve_group(x, g, nbits, p, beta, kappa, iters, early_stop, codes,
                                    C.byref(s), C.byref(z), C.byref(np_), C.byref(lc),
-                                   C.byref(act), _ptr(te), _ptr(ta))
+                                   C.byref(act), C.byref(rose), _ptr(te), _ptr(ta))
         n = np_.value
         return dict(codes=codes, s=float(s.value), z=float(z.value), passes=n,
-                    last_change=lc.value, shrink_active=act.value, err=float(e),
+                    last_change=lc.value, shrink_active=act.value, stopped=rose.value,
+                    err=float(e),
                     trace_S=te[:n].copy(), trace_acc=ta[:n].copy())
 
     # ---- many groups / tensors -------------------------------------------------------------
@@ -148,11 +151,16 @@ class Oracle:
         out = dict(codes=np.empty(w16.size, np.uint8), scale=np.empty(ng, np.uint16),
                    zero_f32=np.empty(ng, np.float32), s=np.empty(ng, np.float32),
                    passes=np.empty(ng, np.uint8), last_change=np.empty(ng, np.uint8),
-                   shrink_active=np.empty(ng, np.uint8))
+                   shrink_active=np.empty(ng, np.uint8), stopped=np.empty(ng, np.uint8))
         self.L.hqo_solve_groups(w16, ng, g, nbits, p, beta, kappa, iters, early_stop,
                                 out["codes"], out["scale"], out["zero_f32"], _ptr(out["s"]),
                                 _ptr(out["passes"]), _ptr(out["last_change"]),
-                                _ptr(out["shrink_active"]))
+                                _ptr(out["shrink_active"]), _ptr(out["stopped"]))
+        # Evaluations needed by a solver that leaves a group once its zero repeats exactly
+        # (every later iteration would be identical): all of them if the loop ended on a
+        # rise, else one per change of the zero plus the initial one.
+        out["evals_needed"] = np.where(out["stopped"] == 1, out["passes"],
+                                       out["last_change"].astype(np.int32) + 1).astype(np.uint8)
         return out
 
     def zero_requant(self, z):

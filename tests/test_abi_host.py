@@ -1,0 +1,103 @@
+"""The C ABI library on the host: it loads, exports what include/hqq.h declares, and rejects
+invalid arguments before any HIP call (so these run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def H():
+    from calibration_free_weight_amd import hqq
+    if not os.path.exists(hqq.LIB_PATH):
+        from calibration_free_weight_amd import build
+        build.build()
+    return hqq
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hqq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hqq_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(H):
+    names = declared_functions()
+    assert len(names) >= 9
+    L = H.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(H.EXPORTS) == names
+
+
+def test_packed_bytes(H):
+    f = H.hqq_packed_bytes
+    assert f(0, 4) == 0 and f(1, 4) == 1 and f(2, 4) == 1 and f(3, 4) == 2
+    assert f(16, 2) == 4 and f(17, 2) == 5 and f(8, 1) == 1 and f(9, 1) == 2
+    assert f(10, 3) == 4 and f(11, 3) == 8 and f(1, 3) == 4 and f(5, 8) == 5
+    assert f(10, 5) == 0
+
+
+def _job(H, **kw):
+    base = dict(W=0x1000, rows=64, cols=256, nbits=4, group_size=64, axis=1, p=0.7, beta=1.0,
+                kappa=1.01, iters=20, early_stop=1, zero_bits=8, packed=0x2000, scale=0x3000,
+                zero=0x4000, zero_meta=0x5000, passes=None)
+    base.update(kw)
+    return H.hqq_job(**base)
+
+
+BAD = [
+    (dict(nbits=5), 1), (dict(nbits=0), 1), (dict(axis=0), 2), (dict(axis=2), 1),
+    (dict(group_size=48), 1), (dict(group_size=0), 1), (dict(group_size=8, cols=256), 2),
+    (dict(p=0.0), 1), (dict(p=1.5), 1), (dict(p=float("nan")), 1), (dict(beta=0.0), 1),
+    (dict(kappa=-1.0), 1), (dict(iters=-1), 1), (dict(iters=255), 1), (dict(early_stop=2), 1),
+    (dict(zero_bits=4), 1), (dict(W=None), 1), (dict(zero_meta=None), 1),
+    (dict(W=0x1002), 1), (dict(packed=0x2008), 1), (dict(rows=-1), 1),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD, ids=[str(b[0]) for b in BAD])
+def test_invalid_arguments_rejected(H, kw, status):
+    L = H.lib()
+    j = _job(H, **kw)
+    st = L.hqq_quantize_batch(C.byref(j), 1, None, 0, None)
+    assert st == status
+    assert L.hqq_last_error().decode() != ""
+    assert H.hqq_status_string(st) != "unknown status"
+    arr = (H.hqq_job * 1)(j)
+    assert L.hqq_workspace_bytes(arr, 1) == 2 ** 64 - 1
+
+
+def test_workspace_sizing_and_check(H):
+    L = H.lib()
+    j8 = _job(H)
+    arr = (H.hqq_job * 1)(j8)
+    need = L.hqq_workspace_bytes(arr, 1)
+    ng = 64 * 256 // 64
+    assert need >= 4 * ng and need % 256 == 0
+    assert L.hqq_quantize_batch(C.byref(j8), 1, None, 0, None) == H.HQQ_ERR_WORKSPACE
+    assert L.hqq_quantize_batch(C.byref(j8), 1, C.c_void_p(0x100000), need - 1, None) == \
+        H.HQQ_ERR_WORKSPACE
+    assert L.hqq_quantize_batch(C.byref(j8), 1, C.c_void_p(0x100010), need, None) == \
+        H.HQQ_ERR_ARG                                   # misaligned workspace
+    j16 = _job(H, zero_bits=16, zero_meta=None)
+    assert L.hqq_workspace_bytes((H.hqq_job * 1)(j16), 1) == 0
+    # empty tensors are valid and need nothing
+    je = _job(H, rows=0, W=None, packed=None, scale=None, zero=None, zero_meta=None)
+    assert L.hqq_workspace_bytes((H.hqq_job * 1)(je), 1) == 0
+    assert L.hqq_quantize_batch(C.byref(je), 1, None, 0, None) == H.HQQ_OK
+
+
+def test_other_entry_points_validate(H):
+    L = H.lib()
+    assert L.hqq_pack(None, 10, 4, None, None) == H.HQQ_ERR_ARG
+    assert L.hqq_pack(C.c_void_p(0x1000), 10, 6, C.c_void_p(0x2000), None) == H.HQQ_ERR_ARG
+    assert L.hqq_pack(C.c_void_p(0x1000), 0, 4, None, None) == H.HQQ_OK
+    assert L.hqq_unpack(C.c_void_p(0x1001), 10, 3, C.c_void_p(0x2000), None) == H.HQQ_ERR_ARG
+    assert L.hqq_dequantize(C.c_void_p(0x1000), C.c_void_p(0x2000), C.c_void_p(0x3000), None,
+                            4, 64, 4, 64, 1, 8, C.c_void_p(0x4000), None) == H.HQQ_ERR_ARG
+    assert L.hqq_dequantize(None, None, None, None, 4, 64, 4, 64, 0, 16, None, None) == \
+        H.HQQ_ERR_UNSUPPORTED

@@ -1,0 +1,177 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle. Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+from tests.conftest import has_gpu
+from tests.gpu_util import compare, u16, u8, weights
+
+pytestmark = pytest.mark.gpu
+
+if has_gpu():
+    from calibration_free_weight_amd import hqq
+
+RNG = np.random.default_rng(2024)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not has_gpu():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def run(W, nbits, g, zero_bits=16, passes=True, **params):
+    out = hqq.quantize(W, nbits, g, zero_bits=zero_bits, passes=passes, **params)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# pack / unpack: bit-exact
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4, 8])
+def test_pack_unpack_bitexact(O, dev, nbits):
+    for n in [1, 9, 10, 11, 15, 16, 17, 31, 33, 1000, 4097, 65539]:
+        print(f"pack nbits={nbits} n={n}", flush=True)
+        codes = RNG.integers(0, 1 << nbits, n).astype(np.uint8)
+        ct = torch.from_numpy(codes).to(dev)
+        nb = hqq.hqq_packed_bytes(n, nbits)
+        packed = torch.full((nb + 16,), 0xAB, dtype=torch.uint8, device=dev)
+        hqq.hqq_pack(ct, n, nbits, packed)
+        back = torch.zeros(n + 8, dtype=torch.uint8, device=dev)
+        hqq.hqq_unpack(packed, n, nbits, back)
+        torch.cuda.synchronize()
+        p = u8(packed)
+        assert np.array_equal(p[:nb], O.pack(codes, nbits))
+        assert np.all(p[nb:] == 0xAB), "pack wrote past the packed size"
+        b = u8(back)
+        assert np.array_equal(b[:n], codes) and np.all(b[n:] == 0)
+
+
+# ---------------------------------------------------------------------------------------
+# quantize: every bit width x group size x zero storage, several blocks and a ragged tail
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("zero_bits", [16, 8])
+@pytest.mark.parametrize("g", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4, 8])
+def test_quantize_matches_oracle(O, dev, nbits, g, zero_bits):
+    rows, cols = 67, g * 20          # 1340 groups: several blocks, last one partial
+    print(f"quantize {rows}x{cols} nbits={nbits} g={g} zero={zero_bits}", flush=True)
+    W = weights(rows, cols, 100 * nbits + g + zero_bits, dev)
+    out = run(W, nbits, g, zero_bits)
+    compare(O, W, out, nbits, g, zero_bits, label=f"b{nbits} g{g} z{zero_bits}")
+
+
+@pytest.mark.parametrize("nbits,g", [(4, 64), (2, 16), (3, 64)])
+def test_no_early_stop_and_rtn(O, dev, nbits, g):
+    W = weights(32, 2048, 5 + nbits, dev)
+    for params in ({"iters": 0}, {"early_stop": False}, {"iters": 5}, {"iters": 254}):
+        print(f"params {params}", flush=True)
+        out = run(W, nbits, g, **params)
+        compare(O, W, out, nbits, g, 16, params=params, label=str(params))
+
+
+def test_edge_inputs(O, dev):
+    cases = {
+        "constant": torch.full((8, 256), 0.375, dtype=torch.float16),
+        "zeros": torch.zeros(8, 256, dtype=torch.float16),
+        "two_valued": torch.where(torch.rand(8, 256, generator=torch.Generator().manual_seed(1)) < 0.5,
+                                  torch.tensor(-0.0625), torch.tensor(0.1875)).half(),
+        "subnormal_only": (torch.randint(-1023, 1024, (8, 256),
+                                         generator=torch.Generator().manual_seed(2)).float()
+                           * 2.0 ** -24).half(),
+        "huge": (torch.randn(8, 256, generator=torch.Generator().manual_seed(3)) * 8000).half(),
+        "one_group": torch.randn(1, 16, generator=torch.Generator().manual_seed(4)).half(),
+    }
+    for name, Wc in cases.items():
+        for nbits in (2, 4):
+            print(f"edge {name} nbits={nbits}", flush=True)
+            W = Wc.to(dev)
+            g = 16
+            out = run(W, nbits, g)
+            compare(O, W, out, nbits, g, 16, label=name)
+
+
+def test_empty_tensor(dev):
+    W = torch.empty(0, 64, dtype=torch.float16, device=dev)
+    out = run(W, 4, 64)
+    assert out["scale"].numel() == 0
+
+
+@pytest.mark.parametrize("params", [{"beta": 1e4}, {"p": 1.0}, {"p": 0.5, "beta": 50.0}])
+def test_active_shrink_within_tolerance(O, dev, params):
+    """With a large beta the shrink moves residuals (the pow branch runs): parity is the
+    tolerance bar, not bit equality (binary64 pow differs between libraries in the last bit)."""
+    W = weights(64, 1024, 77, dev)
+    print(f"shrink {params}", flush=True)
+    out = run(W, 4, 64, **params)
+    ref = compare(O, W, out, 4, 64, 16, exact=False, params=params, label=str(params))
+    if params.get("beta", 1.0) > 100:
+        assert ref["shrink_active"].mean() > 0.5
+
+
+# ---------------------------------------------------------------------------------------
+# full-size tensors
+# ---------------------------------------------------------------------------------------
+def test_full_4096x4096_4bit_g64(O, dev):
+    """The single-matrix workload, compared element by element over the whole tensor."""
+    print("full 4096x4096", flush=True)
+    W = weights(4096, 4096, 1_000_003, dev)
+    out = run(W, 4, 64)
+    compare(O, W, out, 4, 64, 16, label="4096x4096")
+
+
+@pytest.mark.parametrize("rows,cols,nbits,g", [(11008, 4096, 4, 128), (4096, 11008, 2, 16),
+                                               (13824, 5120, 2, 32), (8192, 28672, 3, 64)])
+def test_full_size_sampled(O, dev, rows, cols, nbits, g):
+    """Stack-sized tensors with 8-bit zeros: sampled groups against the oracle one by one
+    (codes, scale and the binary32 zero are exact), the 8-bit zeros by their error bound."""
+    print(f"full-size {rows}x{cols} b{nbits} g{g}", flush=True)
+    W = weights(rows, cols, 31 * rows + cols + nbits, dev)
+    out = run(W, nbits, g, zero_bits=8)
+    ng = rows * cols // g
+    idx = np.sort(RNG.choice(ng, 3000, replace=False))
+    idx = np.unique(np.concatenate([idx, [0, ng - 1]]))
+    w16 = u16(W).reshape(ng, g)
+    sub = np.ascontiguousarray(w16[idx])
+    ref = O.solve_groups(sub.reshape(-1), g, nbits)
+    codes = O.unpack(u8(out["packed"]), rows * cols, nbits).reshape(ng, g)[idx]
+    assert np.array_equal(codes.reshape(-1), ref["codes"])
+    assert np.array_equal(u16(out["scale"])[idx], ref["scale"])
+    z32 = out["workspace"][: 4 * ng].view(torch.float32).cpu().numpy()[idx]
+    assert np.array_equal(z32, ref["zero_f32"])
+    meta = u16(out["zero_meta"]).view(np.float16).astype(np.float64)
+    zq = u8(out["zero"])[idx].astype(np.float64)
+    zr = zq * meta[0] + meta[1]
+    err = np.abs(zr - ref["zero_f32"])
+    inner = (zq > 0) & (zq < 255)
+    assert np.all(err[inner] <= 0.5 * meta[0] * (1 + 1e-5))      # half a step of the grid
+    assert np.all(err <= (0.5 + 255 * 2.0 ** -11) * meta[0] + 2.0 ** -10 * abs(meta[1]))
+    assert u8(out["zero"]).max() == 255 and u8(out["zero"]).min() == 0
+    ok = ref["shrink_active"] == 0
+    assert np.array_equal(u8(out["passes"])[idx][ok], ref["evals_needed"][ok])
+
+
+def test_batch_equals_single_calls(O, dev):
+    """One batched call over mixed jobs writes what the single-tensor calls write."""
+    specs = [(256, 1024, 4, 64, 16), (512, 2048, 4, 128, 8), (128, 4096, 2, 16, 8),
+             (64, 1280, 3, 64, 8), (96, 512, 2, 32, 16), (32, 256, 8, 16, 8)]
+    Ws, outs, jobs = [], [], []
+    for i, (r, c, b, g, zb) in enumerate(specs):
+        W = weights(r, c, 900 + i, dev)
+        o = hqq.alloc_outputs(r, c, b, g, zb, dev, passes=True)
+        jobs.append(hqq.make_job(W, b, g, 1, 0.7, 1.0, 1.01, 20, 1, zb, o["packed"], o["scale"],
+                                 o["zero"], o["zero_meta"], o["passes"]))
+        Ws.append(W)
+        outs.append(o)
+    ws = hqq.alloc_workspace(jobs, dev)
+    hqq.hqq_quantize_batch(jobs, ws)
+    torch.cuda.synchronize()
+    for W, o, (r, c, b, g, zb) in zip(Ws, outs, specs):
+        single = run(W, b, g, zb)
+        for k in ("packed", "scale", "zero", "passes"):
+            assert torch.equal(o[k], single[k]), k
+        if zb == 8:
+            assert torch.equal(o["zero_meta"], single["zero_meta"])
+        compare(O, W, o, b, g, zb, label=f"batch b{b} g{g}")

@@ -245,16 +245,22 @@ def test_zero_requant_range_and_roundtrip(O):
     zq, meta = O.zero_requant(z)
     assert zq.min() == 0 and zq.max() == 255
     assert zq[np.argmin(z)] == 0 and zq[np.argmax(z)] == 255
-    m0 = meta[0:1].view(np.float16).astype(np.float32)[0]
-    m1 = meta[1:2].view(np.float16).astype(np.float32)[0]
-    zmin, zmax = z.min(), z.max()
-    step = (zmax - zmin) / 255
-    zr = zq.astype(np.float64) * m0 + m1
-    bound = 0.5 * step + 255 * abs(m0 - step) + abs(m1 - zmin) + 1e-6
-    assert np.max(np.abs(zr - z)) <= bound
-    # constant zeros
+    step = float(meta[0:1].view(np.float16)[0])
+    base = float(meta[1:2].view(np.float16)[0])
+    assert step == float(np.float16((z.max() - z.min()) / np.float32(255)))
+    assert base == float(np.float16(z.min()))
+    zr = zq.astype(np.float64) * step + base
+    inner = (zq > 0) & (zq < 255)
+    assert np.max(np.abs(zr - z)[inner]) <= 0.5 * step * (1 + 1e-5)   # half a step inside
+    assert np.max(np.abs(zr - z)) <= (0.5 + 255 * 2.0 ** -11) * step + abs(base - z.min())
+    # each code is the nearest grid point
+    for k in RNG.integers(0, z.size, 200):
+        d = np.abs(np.arange(256) * step + base - z[k])
+        assert abs(d[zq[k]] - d.min()) <= 1e-6 * step
+    # constant zeros: step 1, everything at the base
     zq, meta = O.zero_requant(np.full(10, 3.25, np.float32))
     assert np.all(zq == 0) and meta[1:2].view(np.float16)[0] == 3.25
+    assert meta[0:1].view(np.float16)[0] == 1.0
 
 
 def test_dequantize_identity_and_formula(O):
