@@ -87,80 +87,113 @@ hqq_status check_job(const hqq_job &j, int idx)
     return HQQ_OK;
 }
 
-// Workspace of one job: binary32 zero staging, the solver's per-block (min, max) and the
-// derived quantizer, each section 256-byte aligned. Nothing for binary16 zeros.
-size_t job_workspace(const hqq_job &j)
-{
-    if (j.zero_bits != 8 || j.rows * j.cols == 0) return 0;
-    const int64_t ng = j.rows * j.cols / j.group_size;
-    const int64_t nb = hqq::solve_blocks(ng, j.group_size, j.nbits);
-    return round_up(sizeof(float) * (size_t)ng) + round_up(sizeof(float2) * (size_t)nb) +
-           round_up(sizeof(float4));
-}
-
 hqq_status device_fail(hipError_t e, const std::string &what)
 {
     return fail(HQQ_ERR_DEVICE, what + ": " + hipGetErrorString(e));
 }
 
-struct JobWs {
-    float *zero32 = nullptr;
-    float2 *partials = nullptr;
-    float4 *quant = nullptr;
+// ---- batch plan ---------------------------------------------------------------------------
+// Non-empty jobs are grouped into launch classes (same nbits, group size and solver
+// parameters); each class is one persistent solver launch over its jobs' tiles. Workspace:
+//   binary32 zero staging of every 8-bit-zero job (first, so a one-job call finds its zeros
+//   at offset 0), the 3-bit boundary stash of every 3-bit job, per-job (min, max) keys, the
+//   device job table and one tile counter per class; each section 256-byte aligned.
+struct Plan {
+    std::vector<hqq::DevJob> table;      // in class order
+    std::vector<int> first;              // first table index of each class
+    std::vector<int64_t> tiles;          // tiles of each class
+    std::vector<const hqq_job *> src;    // host job of each table entry
+    int64_t n_items = 0;                 // finish-kernel items
+    size_t bytes = 0;
+    size_t off_table = 0, off_counters = 0;
 };
 
-JobWs job_ws(const hqq_job &j, char *ws)
+bool same_class(const hqq_job &a, const hqq_job &b)
 {
-    JobWs r;
-    if (j.zero_bits != 8 || j.rows * j.cols == 0) return r;
-    const int64_t ng = j.rows * j.cols / j.group_size;
-    const int64_t nb = hqq::solve_blocks(ng, j.group_size, j.nbits);
-    r.zero32 = reinterpret_cast<float *>(ws);
-    r.partials = reinterpret_cast<float2 *>(ws + round_up(sizeof(float) * (size_t)ng));
-    r.quant = reinterpret_cast<float4 *>(ws + round_up(sizeof(float) * (size_t)ng) +
-                                         round_up(sizeof(float2) * (size_t)nb));
-    return r;
+    return a.nbits == b.nbits && a.group_size == b.group_size && a.p == b.p && a.beta == b.beta &&
+           a.kappa == b.kappa && a.iters == b.iters && a.early_stop == b.early_stop;
 }
 
-hqq_status solve_job(const hqq_job &j, char *ws, hipStream_t stream)
+// Builds the plan; with ws == nullptr only the sizes are computed.
+void make_plan(const hqq_job *jobs, int n_jobs, char *ws, Plan &P)
 {
-    const int64_t n = j.rows * j.cols;
-    if (n == 0) return HQQ_OK;
-    hqq::SolveArgs a{};
-    a.W = static_cast<const uint16_t *>(j.W);
-    a.n_groups = n / j.group_size;
-    a.p = j.p;
-    a.beta0 = j.beta;
-    a.kappa = j.kappa;
-    a.iters = j.iters;
-    a.early_stop = j.early_stop;
-    a.packed = static_cast<uint8_t *>(j.packed);
-    a.scale = static_cast<uint16_t *>(j.scale);
-    a.passes = j.passes;
-    const JobWs w = job_ws(j, ws);
-    if (j.zero_bits == 8) {
-        a.zero32 = w.zero32;
-        a.partials = w.partials;
-    } else {
-        a.zero16 = static_cast<uint16_t *>(j.zero);
+    std::vector<int> order;
+    std::vector<bool> used(n_jobs, false);
+    for (int i = 0; i < n_jobs; ++i) {
+        if (used[i] || jobs[i].rows * jobs[i].cols == 0) continue;
+        P.first.push_back((int)order.size());
+        for (int j = i; j < n_jobs; ++j) {
+            if (!used[j] && jobs[j].rows * jobs[j].cols != 0 && same_class(jobs[i], jobs[j])) {
+                used[j] = true;
+                order.push_back(j);
+            }
+        }
     }
-    hipError_t e = hqq::launch_solve(a, j.nbits, j.group_size, stream);
-    if (e != hipSuccess) return device_fail(e, "solver launch");
-    return HQQ_OK;
+    const int n = (int)order.size();
+    size_t off = 0;
+    std::vector<size_t> z_off(n), s_off(n);
+    for (int t = 0; t < n; ++t) {
+        const hqq_job &j = jobs[order[t]];
+        const int64_t ng = j.rows * j.cols / j.group_size;
+        z_off[t] = off;
+        if (j.zero_bits == 8) off += round_up(sizeof(float) * (size_t)ng);
+    }
+    for (int t = 0; t < n; ++t) {
+        const hqq_job &j = jobs[order[t]];
+        const int64_t ng = j.rows * j.cols / j.group_size;
+        s_off[t] = off;
+        if (j.nbits == 3) off += round_up(sizeof(uint2) * (size_t)ng);
+    }
+    const size_t off_mm = off;
+    off += round_up(sizeof(uint32_t) * 2 * (size_t)(n > 0 ? n : 1));
+    P.off_table = off;
+    off += round_up(sizeof(hqq::DevJob) * (size_t)(n > 0 ? n : 1));
+    P.off_counters = off;
+    off += round_up(sizeof(uint32_t) * (P.first.size() > 0 ? P.first.size() : 1));
+    P.bytes = n > 0 ? off : 0;
+    P.first.push_back(n);
+    int64_t item = 0;
+    for (size_t c = 0; c + 1 < P.first.size(); ++c) {
+        int64_t tile = 0;
+        for (int t = P.first[c]; t < P.first[c + 1]; ++t) {
+            const hqq_job &j = jobs[order[t]];
+            const int64_t ng = j.rows * j.cols / j.group_size;
+            hqq::DevJob d{};
+            d.W = static_cast<const uint16_t *>(j.W);
+            d.packed = static_cast<uint8_t *>(j.packed);
+            d.scale = static_cast<uint16_t *>(j.scale);
+            d.passes = j.passes;
+            d.n_groups = ng;
+            d.tile0 = tile;
+            d.nbits = j.nbits;
+            d.g = j.group_size;
+            d.item0 = item;
+            if (ws) {
+                if (j.zero_bits == 8) {
+                    d.zero32 = reinterpret_cast<float *>(ws + z_off[t]);
+                    d.minmax = reinterpret_cast<uint32_t *>(ws + off_mm) + 2 * t;
+                    d.zq = static_cast<uint8_t *>(j.zero);
+                    d.meta = static_cast<uint16_t *>(j.zero_meta);
+                } else {
+                    d.zero16 = static_cast<uint16_t *>(j.zero);
+                }
+                if (j.nbits == 3) d.stash = reinterpret_cast<uint2 *>(ws + s_off[t]);
+            }
+            if (j.zero_bits == 8 || j.nbits == 3) item += ng;
+            tile += hqq::tiles_for(ng, j.group_size);
+            P.table.push_back(d);
+            P.src.push_back(&j);
+        }
+        P.tiles.push_back(tile);
+    }
+    P.n_items = item;
 }
 
-hqq_status requant_job(const hqq_job &j, char *ws, hipStream_t stream)
+size_t batch_workspace(const hqq_job *jobs, int n_jobs)
 {
-    const int64_t n = j.rows * j.cols;
-    if (n == 0 || j.zero_bits != 8) return HQQ_OK;
-    const int64_t ng = n / j.group_size;
-    const JobWs w = job_ws(j, ws);
-    hipError_t e = hqq::launch_zero_requant(w.zero32, ng, w.partials,
-                                            hqq::solve_blocks(ng, j.group_size, j.nbits),
-                                            w.quant, static_cast<uint8_t *>(j.zero),
-                                            static_cast<uint16_t *>(j.zero_meta), stream);
-    if (e != hipSuccess) return device_fail(e, "zero requantization launch");
-    return HQQ_OK;
+    Plan P;
+    make_plan(jobs, n_jobs, nullptr, P);
+    return P.bytes;
 }
 
 // Validates every job and the workspace; nothing is enqueued on failure.
@@ -168,12 +201,12 @@ hqq_status check_batch(const hqq_job *jobs, int n_jobs, void *workspace, size_t 
 {
     if (n_jobs < 0) return fail(HQQ_ERR_ARG, "n_jobs must be >= 0");
     if (n_jobs > 0 && !jobs) return fail(HQQ_ERR_ARG, "jobs must be non-null");
-    size_t need = 0;
+    if (n_jobs > 65535) return fail(HQQ_ERR_ARG, "at most 65535 jobs per batch");
     for (int i = 0; i < n_jobs; ++i) {
         hqq_status st = check_job(jobs[i], n_jobs > 1 ? i : -1);
         if (st != HQQ_OK) return st;
-        need += job_workspace(jobs[i]);
     }
+    const size_t need = batch_workspace(jobs, n_jobs);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(HQQ_ERR_WORKSPACE, "workspace must hold " + std::to_string(need) + " bytes");
     if (need > 0 && !aligned(workspace, kAlign))
@@ -188,22 +221,48 @@ hqq_status run_batch(const hqq_job *jobs, int n_jobs, void *workspace, size_t wo
 {
     hqq_status st = check_batch(jobs, n_jobs, workspace, workspace_bytes);
     if (st != HQQ_OK) return st;
+    char *ws = static_cast<char *>(workspace);
+    Plan P;
+    make_plan(jobs, n_jobs, ws, P);
+    const int n = (int)P.table.size();
+    if (n == 0) {
+        g_last_error.clear();
+        return HQQ_OK;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    hqq::DevJob *table = reinterpret_cast<hqq::DevJob *>(ws + P.off_table);
+    uint32_t *counters = reinterpret_cast<uint32_t *>(ws + P.off_counters);
+    const int n_classes = (int)P.first.size() - 1;
     if (phases & kSolve) {
-        char *ws = static_cast<char *>(workspace);
-        for (int i = 0; i < n_jobs; ++i) {
-            st = solve_job(jobs[i], ws, s);
-            if (st != HQQ_OK) return st;
-            ws += job_workspace(jobs[i]);
+        for (int o = 0; o < n; o += hqq::kFillJobs) {
+            hqq::FillArgs f{};
+            f.n = n - o < hqq::kFillJobs ? n - o : hqq::kFillJobs;
+            f.offset = o;
+            f.counters = counters;
+            f.n_counters = n_classes;
+            for (int i = 0; i < f.n; ++i) f.jobs[i] = P.table[o + i];
+            hipError_t e = hqq::launch_fill(f, table, s);
+            if (e != hipSuccess) return device_fail(e, "job table launch");
+        }
+        for (int c = 0; c < n_classes; ++c) {
+            const hqq_job &j = *P.src[P.first[c]];
+            hqq::StreamArgs a{};
+            a.jobs = table + P.first[c];
+            a.n_jobs = P.first[c + 1] - P.first[c];
+            a.n_tiles = P.tiles[c];
+            a.p = j.p;
+            a.beta0 = j.beta;
+            a.kappa = j.kappa;
+            a.iters = j.iters;
+            a.early_stop = j.early_stop;
+            a.counter = counters + c;
+            hipError_t e = hqq::launch_stream(a, j.nbits, j.group_size, s);
+            if (e != hipSuccess) return device_fail(e, "solver launch");
         }
     }
     if (phases & kRequant) {
-        char *ws = static_cast<char *>(workspace);
-        for (int i = 0; i < n_jobs; ++i) {
-            st = requant_job(jobs[i], ws, s);
-            if (st != HQQ_OK) return st;
-            ws += job_workspace(jobs[i]);
-        }
+        hipError_t e = hqq::launch_finish(table, n, P.n_items, s);
+        if (e != hipSuccess) return device_fail(e, "zero requantization launch");
     }
     g_last_error.clear();
     return HQQ_OK;
@@ -218,12 +277,10 @@ size_t hqq_packed_bytes(int64_t n_codes, int nbits) { return packed_bytes(n_code
 size_t hqq_workspace_bytes(const hqq_job *jobs, int n_jobs)
 {
     if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return SIZE_MAX;
-    size_t total = 0;
-    for (int i = 0; i < n_jobs; ++i) {
+    if (n_jobs > 65535) return SIZE_MAX;
+    for (int i = 0; i < n_jobs; ++i)
         if (check_job(jobs[i], i) != HQQ_OK) return SIZE_MAX;
-        total += job_workspace(jobs[i]);
-    }
-    return total;
+    return batch_workspace(jobs, n_jobs);
 }
 
 hqq_status hqq_quantize_batch(const hqq_job *jobs, int n_jobs, void *workspace,

@@ -16,55 +16,65 @@ __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
 // ---------------------------------------------------------------------------------------
+// After the solve, per batch: 8-bit zero-points and the 3-bit words shared by two groups.
+//
 // 8-bit zero-point [techreport.ngo, "Half-Quadratic Quantization of Large Machine Learning
 // Models", section "Benchmark results / Llama-2": the zero-point is quantized to 8 bit with
 // no further grouping or optimisation]. One min-max affine uint8 round-to-nearest quantizer
 // over all zeros of the tensor, on the grid of its stored binary16 pair:
 //   step = binary16((zmax - zmin)/255) (1 if that is 0), base = binary16(zmin),
 //   zq = clamp(rne((z - base)/step), 0, 255), meta = {step, base}; read back zq*step + base.
+// The solver leaves each tensor's (zmin, zmax) as order-preserving integer keys.
 // ---------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(1024) zero_minmax_kernel(const float2 *partials, int64_t n,
-                                                           float4 *quant, uint16_t *meta)
+__device__ __forceinline__ float unkey(uint32_t k)
 {
-    __shared__ float2 red[16];
-    float lo = INFINITY, hi = -INFINITY;
-    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-        float2 p = partials[i];
-        lo = fminf(lo, p.x);
-        hi = fmaxf(hi, p.y);
-    }
-    for (int o = 1; o < 64; o <<= 1) {
-        lo = fminf(lo, __shfl_xor(lo, o));
-        hi = fmaxf(hi, __shfl_xor(hi, o));
-    }
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(lo, hi);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) {
-            lo = fminf(lo, red[w].x);
-            hi = fmaxf(hi, red[w].y);
-        }
-        uint16_t h_step = f2h((hi - lo) / 255.0f);
-        float step = h2f(h_step);
-        if (!(step > 0.0f)) {
-            h_step = 0x3c00;                        // binary16 1.0
-            step = 1.0f;
-        }
-        const uint16_t h_base = f2h(lo);
-        *quant = make_float4(step, h2f(h_base), lo, hi);
-        meta[0] = h_step;
-        meta[1] = h_base;
-    }
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-__global__ void __launch_bounds__(256) zero_quant_kernel(const float *z, int64_t n,
-                                                         const float4 *quant, uint8_t *zq)
+constexpr int kFinishPerThread = 8;
+
+__global__ void __launch_bounds__(256) finish_kernel(const DevJob *table, int n_jobs,
+                                                     int64_t n_items)
 {
-    const float4 qp = *quant;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        float v = rintf((z[i] - qp.y) / qp.x);
-        zq[i] = (uint8_t)fminf(fmaxf(v, 0.0f), 255.0f);
+    __shared__ int job_sh;
+    const int64_t base = (int64_t)blockIdx.x * 256 * kFinishPerThread;
+    if (threadIdx.x == 0) {
+        int lo = 0, hi = n_jobs - 1;                // last job with item0 <= base
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (table[mid].item0 <= base) lo = mid;
+            else hi = mid - 1;
+        }
+        job_sh = lo;
+    }
+    __syncthreads();
+    int j = job_sh;
+    for (int r = 0; r < kFinishPerThread; ++r) {
+        const int64_t item = base + (int64_t)r * 256 + threadIdx.x;
+        if (item >= n_items) break;
+        while (j + 1 < n_jobs && table[j + 1].item0 <= item) ++j;
+        const DevJob &J = table[j];
+        const int64_t i = item - J.item0;
+        if (J.zq) {
+            const float zmin = unkey(J.minmax[0]), zmax = unkey(J.minmax[1]);
+            uint16_t h_step = f2h((zmax - zmin) / 255.0f);
+            float step = h2f(h_step);
+            if (!(step > 0.0f)) {
+                h_step = 0x3c00;                    // binary16 1.0
+                step = 1.0f;
+            }
+            const uint16_t h_base = f2h(zmin);
+            const float v = rintf((J.zero32[i] - h2f(h_base)) / step);
+            J.zq[i] = (uint8_t)fminf(fmaxf(v, 0.0f), 255.0f);
+            if (i == 0) {
+                J.meta[0] = h_step;
+                J.meta[1] = h_base;
+            }
+        }
+        if (J.stash && i >= 1 && (i * J.g) % 10 != 0) {
+            const int64_t w = i * J.g / 10;
+            reinterpret_cast<uint32_t *>(J.packed)[w] = J.stash[i - 1].x | J.stash[i].y;
+        }
     }
 }
 
@@ -167,17 +177,13 @@ unsigned grid_for(int64_t items, int per_block)
 
 }  // namespace
 
-hipError_t launch_zero_requant(const float *zero32, int64_t n_groups, const float2 *partials,
-                               int64_t n_partials, float4 *quant, uint8_t *zq, uint16_t *meta,
-                               hipStream_t stream)
+hipError_t launch_finish(const DevJob *table, int n_jobs, int64_t n_items, hipStream_t stream)
 {
-    if (n_groups == 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_minmax_kernel, dim3(1), dim3(1024), 0, stream, partials,
-                       n_partials, quant, meta);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(zero_quant_kernel, dim3(grid_for(n_groups, 256 * 4)), dim3(256), 0,
-                       stream, zero32, n_groups, (const float4 *)quant, zq);
+    if (n_items == 0 || n_jobs == 0) return hipSuccess;
+    const int64_t per_block = 256 * kFinishPerThread;
+    const int64_t blocks = (n_items + per_block - 1) / per_block;
+    hipLaunchKernelGGL(finish_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, table, n_jobs,
+                       n_items);
     return hipGetLastError();
 }
 

@@ -8,30 +8,50 @@ namespace hqq {
 
 constexpr int kMaxIters = 254;      // passes are counted in uint8 (1..iters+1)
 
-// Arguments of one solver launch (one tensor).
-struct SolveArgs {
-    const uint16_t *W;              // binary16 bits, n_groups * G elements
+// One tensor as the device kernels see it (the job table lives in the caller's workspace).
+struct DevJob {
+    const uint16_t *W;          // binary16 weights, n_groups * g elements
+    uint8_t *packed;            // packed code stream
+    uint16_t *scale;            // binary16 [n_groups]
+    uint16_t *zero16;           // binary16 zeros, or nullptr for 8-bit zeros
+    float *zero32;              // binary32 zero staging for 8-bit zeros, or nullptr
+    uint8_t *passes;            // nullable
+    uint2 *stash;               // 3-bit: partial boundary words per group, or nullptr
+    uint32_t *minmax;           // 8-bit zeros: order-preserving keys {min, max}
+    uint8_t *zq;                // 8-bit zeros out
+    uint16_t *meta;             // 8-bit zeros: binary16 {step, base} out
     int64_t n_groups;
-    float p, beta0, kappa;
-    int iters, early_stop;
-    uint8_t *packed;                // packed code stream
-    uint16_t *scale;                // binary16 [n_groups]
-    uint16_t *zero16;               // binary16 zeros (zero_bits == 16) or nullptr
-    float *zero32;                  // binary32 zero staging (zero_bits == 8) or nullptr
-    uint8_t *passes;                // nullable
-    float2 *partials;               // per-block (min, max) of zero32, or nullptr
+    int64_t tile0;              // first tile of this job in its launch class
+    int64_t item0;              // first item of this job in the finish kernel's index space
+    int32_t nbits, g;
 };
 
-// Number of blocks the solver launch uses for n_groups groups of size g at nbits.
-int64_t solve_blocks(int64_t n_groups, int g, int nbits);
+// One persistent solver launch: jobs that share nbits, g and the solver parameters.
+struct StreamArgs {
+    const DevJob *jobs;         // this class's jobs, ordered by tile0
+    int n_jobs;
+    int64_t n_tiles;
+    float p, beta0, kappa;
+    int iters, early_stop;
+    uint32_t *counter;          // tile claim counter, zero before the launch
+    uint32_t chunk;             // tiles per claim
+};
 
-hipError_t launch_solve(const SolveArgs &a, int nbits, int g, hipStream_t stream);
+constexpr int kFillJobs = 24;   // job descriptors per table-fill launch (kernel arguments)
+struct FillArgs {
+    DevJob jobs[kFillJobs];
+    int n, offset;
+    uint32_t *counters;         // zeroed by the launch with offset 0
+    int n_counters;
+};
 
-// 8-bit zero requantization: reduce the solver's per-block partials to the tensor's
-// (zmin, zmax), derive the affine uint8 quantizer and the binary16 meta pair, then quantize.
-hipError_t launch_zero_requant(const float *zero32, int64_t n_groups, const float2 *partials,
-                               int64_t n_partials, float4 *quant, uint8_t *zq,
-                               uint16_t *meta, hipStream_t stream);
+// Launch configuration of the solver for one class.
+int64_t tiles_for(int64_t n_groups, int g);
+hipError_t launch_fill(const FillArgs &f, DevJob *table, hipStream_t stream);
+hipError_t launch_stream(const StreamArgs &a, int nbits, int g, hipStream_t stream);
+// 8-bit zeros (per job min/max from the solver, then uint8 codes + meta) and 3-bit boundary
+// words, over all jobs of a batch: items [0, n_items) map to jobs by DevJob::item0.
+hipError_t launch_finish(const DevJob *table, int n_jobs, int64_t n_items, hipStream_t stream);
 
 hipError_t launch_dequant(const uint8_t *packed, const uint16_t *scale, const void *zero,
                           const uint16_t *meta, int64_t n, int nbits, int g, int zero_bits,

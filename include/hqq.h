@@ -76,10 +76,10 @@ typedef struct hqq_job {
  * ceil(n*nbits/8) for 8/4/2/1 bits, 4*ceil(n/10) for 3 bits. */
 size_t hqq_packed_bytes(int64_t n_codes, int nbits);
 
-/* Workspace bytes hqq_quantize_batch needs for these jobs (host array). The workspace holds
- * the device copy of the job table, binary32 zero staging for 8-bit zero requantization and
- * the per-tensor reductions (0 when every job stores binary16 zeros). Returns SIZE_MAX if
- * a job is invalid; the quantize call then reports why. */
+/* Workspace bytes hqq_quantize_batch needs for these jobs (host array): the device copy of
+ * the job table and its work counters, binary32 zero staging and per-tensor (min, max) for
+ * 8-bit zero requantization, and the words that 3-bit groups share (0 if every tensor is
+ * empty). Returns SIZE_MAX if a job is invalid; the quantize call then reports why. */
 size_t hqq_workspace_bytes(const hqq_job *jobs, int n_jobs);
 
 /* Quantize one tensor [TR "Outlier-aware optimization without gradients"].
@@ -91,9 +91,9 @@ size_t hqq_workspace_bytes(const hqq_job *jobs, int n_jobs);
  * (early_stop). Per-element arithmetic is exact; the zero is rounded to binary32 at each
  * update. Outputs: packed codes, scale = binary16(1/s), zero (see hqq_job), passes.
  * workspace: device buffer (256-byte aligned) of at least hqq_workspace_bytes() for this one
- * job; 0 bytes are needed for zero_bits == 16 and workspace may then be NULL. With
- * zero_bits == 8 its first 4*n_groups bytes hold, after the call, the binary32 zeros the
- * solver returned (before 8-bit requantization). */
+ * job (it holds the device job table; NULL only for an empty tensor). With zero_bits == 8
+ * its first 4*n_groups bytes hold, after the call, the binary32 zeros the solver returned
+ * (before 8-bit requantization). */
 hqq_status hqq_quantize(const void *W, int64_t rows, int64_t cols, int nbits, int group_size,
                         int axis, float p, float beta, float kappa, int iters, int early_stop,
                         int zero_bits, void *packed, void *scale, void *zero, void *zero_meta,

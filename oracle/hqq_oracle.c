@@ -154,7 +154,7 @@ double hqo_eval(const double *x, int g, float s, float z, int qmax, double *q, d
 }
 
 /* Min-max affine initialisation of one group. Reading (the pages do not spell out the
- * start point): scale s = qmax / (max - min) and zero z = -min * s, both binary32 operations,
+ * start point): scale s = qmax / (max - min) and zero z = 0 - min * s, binary32 operations,
  * so iteration 0 is plain round-to-nearest; a constant group (max == min) takes s = 1,
  * z = -min. The zero is not rounded to an integer or clamped: it is the continuous variable
  * the solver optimises [TR]. */
@@ -168,7 +168,7 @@ void hqo_init(const double *x, int g, int qmax, float *s_out, float *z_out)
     float rng = mx - mn;
     float s = rng > 0.0f ? (float)qmax / rng : 1.0f;
     *s_out = s;
-    *z_out = -(mn * s);
+    *z_out = 0.0f - mn * s;                         /* +0 (not -0) when min is a zero */
 }
 
 enum { HQO_MAX_G = 4096 };

@@ -84,7 +84,12 @@ def test_workspace_sizing_and_check(H):
     assert L.hqq_quantize_batch(C.byref(j8), 1, C.c_void_p(0x100010), need, None) == \
         H.HQQ_ERR_ARG                                   # misaligned workspace
     j16 = _job(H, zero_bits=16, zero_meta=None)
-    assert L.hqq_workspace_bytes((H.hqq_job * 1)(j16), 1) == 0
+    n16 = L.hqq_workspace_bytes((H.hqq_job * 1)(j16), 1)
+    assert 0 < n16 < need and n16 % 256 == 0
+    assert L.hqq_quantize_batch(C.byref(j16), 1, None, 0, None) == H.HQQ_ERR_WORKSPACE
+    # two jobs of one class need one table of two entries, not two workspaces
+    two = (H.hqq_job * 2)(j16, j16)
+    assert L.hqq_workspace_bytes(two, 2) < 2 * n16 + 512
     # empty tensors are valid and need nothing
     je = _job(H, rows=0, W=None, packed=None, scale=None, zero=None, zero_meta=None)
     assert L.hqq_workspace_bytes((H.hqq_job * 1)(je), 1) == 0
