@@ -223,7 +223,6 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
     __shared__ uint32_t st_gidx[NS];   // group index within its tensor
     __shared__ uint16_t st_job[NS];    // job index within the launch class
     __shared__ uint8_t st_t[NS];       // index of the next zero update (1-based)
-    __shared__ uint8_t st_np[NS];      // evaluations run
     __shared__ uint8_t st_fl[NS];      // bit 0: Sb/Db exact; bits 1-2: exact-path work
     __shared__ uint8_t rings[4 * C::RC];   // slot rings: active, finished, exact-pending, free
     uint8_t *const ring_act = rings, *const ring_fin = rings + C::RC,
@@ -245,7 +244,7 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
     }
     for (int i = lane; i < NS; i += 64) ring_free[i] = (uint8_t)i;
     __syncthreads();
-    const double tau_last = a.iters > 0 ? (double)tau[a.iters - 1] * (1.0 - 1e-6) : 0.0;
+    const float tau_min = a.iters > 0 ? tau[a.iters - 1] * (1.0f - 4e-6f) : 0.0f;
     const double pm1 = (double)a.p - 1.0;
 
     uint32_t act_h = 0, act_n = 0, fin_h = 0, fin_n = 0, exq_h = 0, exq_n = 0, fre_h = 0, fre_n = NS;
@@ -313,22 +312,24 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
     auto advance = [&](uint8_t slot, float s, float zb, float Qb, float Db, bool sbx) -> uint8_t {
         const int t = st_t[slot];
         if (t > a.iters) return kFinished;
-        // dead zone of the shrink: max|r| = max|u - q|/s <= beta^(-1/(2-p)) (with margin)
-        const double dmax = sbx ? (double)Db : (double)Db + (double)(0.5f - C::kThr);
-        const double sdm = (double)s * (1.0 - 1e-6);
-        if (!(dmax <= (double)tau[t - 1] * sdm)) {
+        // Dead zone of the shrink: max|r| = max|u - q|/s <= beta^(-1/(2-p)), tested with a
+        // relative margin of 4e-6 that covers the binary32 rounding of the products. The
+        // smallest threshold (the last beta) decides most groups at once, for this and every
+        // later iteration.
+        const float dmax = sbx ? Db : Db + (0.5f - C::kThr);
+        const bool dead_all = dmax <= tau_min * s;
+        if (!dead_all && !(dmax <= tau[t - 1] * (s * (1.0f - 4e-6f)))) {
             if (leader) st_fl[slot] = (uint8_t)((sbx ? 1 : 0) | (kShrink << 1));
             return kExact;                           // the shrink may move residuals
         }
         const float zn = (float)(((double)Qb - st_sxs[slot]) * (1.0 / G));
-        const float beta = st_beta[slot] * a.kappa;
-        if (zn == zb && dmax <= tau_last * (double)s) {   // exact fixed point
+        if (zn == zb && dead_all) {                  // exact fixed point
             if (leader) st_zb[slot] = zn;
             return kFinished;
         }
         if (leader) {
             st_z[slot] = zn;
-            st_beta[slot] = beta;
+            st_beta[slot] = st_beta[slot] * a.kappa;
             st_t[slot] = (uint8_t)(t + 1);
         }
         return kActive;
@@ -415,7 +416,6 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
                     st_gidx[slot] = (uint32_t)(pf_g0 + k);
                     st_job[slot] = (uint16_t)pf_job;
                     st_t[slot] = 1;
-                    st_np[slot] = 1;
                     st_fl[slot] = sbx ? 1 : 0;
                 }
                 out = advance(slot, s, z0, Q, D, sbx);
@@ -516,7 +516,8 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
                     gbl(J.scale)[gidx] = f2h(1.0f / s);
                     if (J.zero16) gbl(J.zero16)[gidx] = f2h(zb);
                     if (J.zero32) gbl(J.zero32)[gidx] = zb;
-                    if (J.passes) gbl(J.passes)[gidx] = st_np[slot];
+                    // evaluations run = index of the next update when the group stops
+                    if (J.passes) gbl(J.passes)[gidx] = st_t[slot];
                 }
                 if constexpr (NBITS == 3) {
 #pragma unroll
@@ -644,14 +645,13 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
             act_h = (act_h + n) & RM;
             act_n -= n;
             uint32_t xr[W];
-            float z = 0.f, s = 1.f;
-            double Sb = 0.0;
+            float z = 0.f, s = 1.f, Sb = 0.f;
             uint8_t fl = 0;
             bool clampfree = true;
             if (valid) {
                 z = st_z[slot];
                 s = st_s[slot];
-                Sb = st_Sb[slot];
+                Sb = (float)st_Sb[slot];
                 fl = st_fl[slot];
                 const uint32_t mm = st_mnmx[slot];
                 const uint4 *src = reinterpret_cast<const uint4 *>(xs + slot * G + sub * E);
@@ -676,7 +676,6 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
                 S = addf_k<K>(S);
                 Q = addf_k<K>(Q);
                 D = maxf_k<K>(D);
-                if (leader) st_np[slot] = (uint8_t)(st_np[slot] + 1);
                 bool accept = false;
                 if (D >= C::kThr) {
                     if (leader) st_fl[slot] = (uint8_t)((fl & 1) | (kDecide << 1));
@@ -684,13 +683,15 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
                 } else if (!a.early_stop) {
                     accept = true;
                 } else {
-                    // |S - S_exact| bounds; clamped elements may sit above 2^NBITS where the
-                    // binary32 ulp is larger, so a clamped pass takes a wider bound.
-                    const double em = any_clamp ? 4.0 * C::kElemErr : C::kElemErr;
-                    const double m = em + (double)S * 0x1p-18 +
-                                     ((fl & 1) ? 0.0 : 4.0 * C::kElemErr + Sb * 0x1p-18);
-                    if ((double)S > Sb + m) out = kFinished;
-                    else if ((double)S < Sb - m) accept = true;
+                    // |S - S_exact| bounds (binary32 sums: G half-ulps of u plus the relative
+                    // summation error; clamped elements may sit above 2^NBITS where the ulp is
+                    // larger, so a clamped pass takes a wider bound). The margins are far above
+                    // the binary32 rounding of this comparison itself.
+                    const float em = any_clamp ? 4.0f * (float)C::kElemErr : (float)C::kElemErr;
+                    const float m = em + S * 0x1p-18f +
+                                    ((fl & 1) ? 0x1p-18f * Sb : 4.0f * (float)C::kElemErr + Sb * 0x1p-18f);
+                    if (S > Sb + m) out = kFinished;
+                    else if (S < Sb - m) accept = true;
                     else {
                         if (leader) st_fl[slot] = (uint8_t)((fl & 1) | (kDecide << 1));
                         out = kExact;
