@@ -20,6 +20,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+# Plain (non-packed) fp32 VALU issue rate: 64 lane operations per clock on each of the 256
+# compute units at 2.4 GHz, 39.32e12/s. The published 157.3 TFLOP/s fp32 vector peak counts an
+# FMA as two flops on packed two-lane instructions, which this library does not emit.
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 METRIC = "fp16 weight GB/s quantized (% HBM peak); seconds per Llama-2-7B-shaped stack"
 
 
@@ -35,6 +39,52 @@ def alg_bytes(spec) -> float:
     ng = n // spec.group_size
     zb = 2 if spec.zero_bits == 16 else 1
     return 2.0 * n + hqq.hqq_packed_bytes(n, spec.nbits) + ng * (2 + zb)
+
+
+SOLVER_SOURCE = os.path.join(ROOT, "calibration_free_weight_amd", "csrc", "hqq_stream.hip")
+
+
+def source_digest() -> str:
+    import hashlib
+    with open(SOLVER_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: int):
+    """HBM bytes per solver launch from the committed counter summary of this workload, or
+    None when there is none or the solver source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_stream_kernel_workload{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("solver source sha256") != source_digest():
+        return None
+    return float(fields["hbm bytes per launch"])
+
+
+def alg_ops_per_weight(mean_passes: float) -> float:
+    """Algorithmic fp32 operations per weight: each evaluation of the quantizer costs 5 per
+    element (fma, round, clamp; residual, absolute sum) and each zero update 3 (sub, fma,
+    add); `mean_passes` counts evaluations, the first included."""
+    return 5.0 * mean_passes + 3.0 * (mean_passes - 1.0)
+
+
+def copy_probe(mib: int, dev):
+    """A plain copy of known size (binary16 negation: reads and writes `mib` MiB once), run a
+    few times so that a counter pass over this program can scale its byte counters."""
+    import torch
+    n = mib * (1 << 20) // 2
+    a = torch.ones(n, dtype=torch.float16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def cpu_baseline(specs, weights, seconds):
@@ -76,6 +126,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -87,6 +139,8 @@ def main():
     from calibration_free_weight_amd import hqq
 
     dev = torch.device("cuda:0")
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib, dev)
     specs = synth.workload(args.workload)
     n_weights = sum(s.numel for s in specs)
     log(f"bench: workload {args.workload} ({synth.WORKLOAD_NAMES[args.workload]}), "
@@ -139,6 +193,19 @@ def main():
     t1 = time.perf_counter()
     log("bench: timed steps done")
 
+    # Mean evaluations per group, from the solver's own per-group counts (untimed run).
+    n_pass, n_groups = 0, 0
+    for s, j in zip(specs, job_sets[0]):
+        ng = s.numel // s.group_size
+        pb = torch.empty(ng, dtype=torch.uint8, device=dev)
+        j.passes = pb.data_ptr()
+        hqq.hqq_quantize_batch([j], ws, stream.cuda_stream)
+        n_pass += int(pb.sum(dtype=torch.int64).item())
+        n_groups += ng
+        j.passes = None
+        del pb
+    mean_passes = n_pass / n_groups
+
     sec_per_step = (t1 - t0) / args.steps
     value = 2.0 * n_weights / sec_per_step / 1e9
     solve_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
@@ -147,7 +214,18 @@ def main():
     launches = len(classes)
     kernel = ", ".join(f"stream_kernel<{b},{g}>" for b, g in classes)
     bytes_step = sum(alg_bytes(s) for s in specs)
-    achieved = bytes_step / (solve_ms * 1e-3) / 1e9
+    launch_s = solve_ms * 1e-3 / launches
+    bytes_launch = bytes_step / launches
+    ops_launch = n_weights * alg_ops_per_weight(mean_passes) / launches
+    hbm = {"achieved": round(bytes_launch / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "floor_ms": round(bytes_launch / HBM_PEAK_GBS / 1e6, 4)}
+    hbm["frac"] = round(hbm["achieved"] / HBM_PEAK_GBS, 4)
+    alu = {"achieved": round(ops_launch / launch_s / 1e12, 3), "peak": round(ALU_PEAK_TOPS, 3),
+           "unit": "Top/s", "floor_ms": round(ops_launch / ALU_PEAK_TOPS / 1e9, 4)}
+    alu["frac"] = round(alu["achieved"] / ALU_PEAK_TOPS, 4)
+    # The binding roof is the one with the longer floor.
+    bound, main = ("alu", alu) if alu["floor_ms"] > hbm["floor_ms"] else ("hbm", hbm)
+    traffic = measured_traffic(args.workload)
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -166,11 +244,14 @@ def main():
                    "early_stop": True},
         "seconds_per_stack": round(sec_per_step, 6),
         "pct_hbm_peak": round(100.0 * bytes_step / sec_per_step / 1e9 / HBM_PEAK_GBS, 3),
-        "roofline": {"bound": "hbm", "kernel": kernel,
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "launch_ms": round(solve_ms / launches, 5),
-                     "bytes_per_launch": round(bytes_step / launches, 1)},
+        "roofline": {"bound": bound, "kernel": kernel, "achieved": main["achieved"],
+                     "peak": main["peak"], "unit": main["unit"], "frac": main["frac"],
+                     "traffic": traffic,
+                     "launch_ms": round(launch_s * 1e3, 5),
+                     "bytes_per_launch": round(bytes_launch, 1),
+                     "ops_per_launch": round(ops_launch, 1),
+                     "mean_passes": round(mean_passes, 4),
+                     "hbm": hbm, "alu": alu},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host")
