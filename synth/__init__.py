@@ -24,9 +24,9 @@ _CHUNK = 1 << 27  # elements generated per step (6 normals each)
 PROJ = ("q", "k", "v", "o", "gate", "up", "down")
 
 
-def seed_for(config: int, block: int, proj: int) -> int:
-    """Seed of one tensor: 1,000,003*config + 1,009*block + projection index (q..down = 0..6)."""
-    return 1_000_003 * config + 1_009 * block + proj
+def seed_for(workload: int, block: int, proj: int) -> int:
+    """Seed of one tensor: 1,000,003*workload + 1,009*block + projection index (q..down = 0..6)."""
+    return 1_000_003 * workload + 1_009 * block + proj
 
 
 def student_t_weights(rows: int, cols: int, seed: int, device="cpu",
@@ -67,8 +67,8 @@ class TensorSpec:
     def numel(self) -> int:
         return self.rows * self.cols
 
-    def seed(self, config: int) -> int:
-        return seed_for(config, self.block, self.proj)
+    def seed(self, workload: int) -> int:
+        return seed_for(workload, self.block, self.proj)
 
 
 def _stack(n_blocks, hidden, inter, kv_out, attn_bits, attn_g, mlp_bits, mlp_g, zero_bits):
@@ -86,24 +86,24 @@ def _stack(n_blocks, hidden, inter, kv_out, attn_bits, attn_g, mlp_bits, mlp_g, 
     return specs
 
 
-def workload(config: int) -> list[TensorSpec]:
+def workload(number: int) -> list[TensorSpec]:
     """Tensor list of a workload, numbered 1..5:
     1: one 4096x4096 matrix, 4-bit g64, fp16 zero;
     2: Llama-2-7B-shaped stack (32 blocks), 4-bit g128, 8-bit zero;
     3: the same stack, 2-bit g16, 8-bit zero;
     4: Llama-2-13B-shaped stack (40 blocks), attention 4-bit g64 / MLP 2-bit g32, 8-bit zero;
     5: Llama-2-70B-shaped stack (80 blocks, GQA k/v 1024 rows), 3-bit g64, 8-bit zero."""
-    if config == 1:
+    if number == 1:
         return [TensorSpec("w", 0, 0, 4096, 4096, 4, 64, 16)]
-    if config == 2:
+    if number == 2:
         return _stack(32, 4096, 11008, 4096, 4, 128, 4, 128, 8)
-    if config == 3:
+    if number == 3:
         return _stack(32, 4096, 11008, 4096, 2, 16, 2, 16, 8)
-    if config == 4:
+    if number == 4:
         return _stack(40, 5120, 13824, 5120, 4, 64, 2, 32, 8)
-    if config == 5:
+    if number == 5:
         return _stack(80, 8192, 28672, 1024, 3, 64, 3, 64, 8)
-    raise ValueError(f"unknown workload {config}")
+    raise ValueError(f"unknown workload {number}")
 
 
 WORKLOAD_NAMES = {
