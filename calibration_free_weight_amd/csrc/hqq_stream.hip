@@ -1,5 +1,5 @@
-// hqq_stream.hip -- the HQQ group solver for gfx950: persistent waves streaming groups
-// through an LDS pool.
+// hqq_stream.hip -- the HQQ group solver for gfx950: persistent waves in which every lane owns
+// one group, its weights held in registers from the first evaluation to the last.
 //
 // Method [techreport.ngo, "Half-Quadratic Quantization of Large Machine Learning Models",
 // section "Outlier-aware optimization without gradients"; parameters from its section
@@ -29,12 +29,18 @@
 //  * A group whose new zero equals the accepted one, with the shrink dead for every later
 //    beta, is at an exact fixed point: every later iteration repeats it, so it finishes.
 //
-// Scheduling: one wave per workgroup, persistent. The wave claims tiles (GPI consecutive
-// groups of one tensor; 64 lanes x E weights) from a global counter, prefetches the next tile
-// into registers, and keeps up to NS = 3*GPI groups resident in LDS: a ring of active groups
-// (each pass takes up to GPI of them, so lanes stay busy while groups stop at different
-// iterations), a list of finished groups (epilogue in batches of GPI), a list of groups that
-// need the exact path (also batched) and a free list. K = G/E lanes hold one group.
+// Scheduling (one wave per workgroup, persistent):
+//  * PASS: each lane (a lane pair for G = 256) holds one group's weights in VGPRs together
+//    with its solver state, evaluates it at its candidate zero and takes the stop / accept /
+//    next-zero decision itself. No data moves between lanes and nothing touches memory.
+//  * A group that finishes, or whose decision needs the exact path, leaves its lane for a
+//    staging slot in LDS; the lane takes a ready group from LDS in its place (an exchange
+//    when both exist, so the pool can never block).
+//  * Work that is cheaper across lanes runs in batches of GB groups with KB lanes per group
+//    (EB weights per lane): INIT (a prefetched tile of GB groups: min/max, s, z0, exact
+//    sum x*s; the groups become ready), EXACT (binary64 decisions and shrink updates) and
+//    EPILOGUE (codes of the accepted zero, packing, scale and zero stores).
+//  * The next tile's weights are in flight in registers while the wave works.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -44,8 +50,10 @@
 namespace hqq {
 namespace {
 
-enum : uint8_t { kActive = 0, kFinished = 1, kExact = 2 };
-enum : uint8_t { kDecide = 1, kShrink = 2 };         // exact-path work (flags bits 1-2)
+enum : uint32_t { kEmpty = 0, kActive = 1, kHoldFin = 2, kHoldExq = 3 };   // a lane's group
+// Group flags: bit 0 Sb/Db exact, bits 1-2 exact-path work, bit 3 first evaluation pending.
+enum : uint8_t { kSbExact = 1, kFirst = 8 };
+enum : uint8_t { kDecide = 1, kShrink = 2 };
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));   // two binary16 weights
 
 // Global-address-space view of a pointer: global_* instructions count only against vmcnt,
@@ -128,14 +136,21 @@ __device__ __forceinline__ double shrink(double r, double pm1, double beta)
     return r > 0.0 ? m : -m;
 }
 
+
 template <int NBITS, int G>
 struct Cfg {
-    static constexpr int E = G >= 32 ? 32 : 16;     // weights per lane
-    static constexpr int K = G / E;                 // lanes per group
-    static constexpr int GPI = 64 / K;              // groups per pass
-    static constexpr int NS = 3 * GPI;              // resident groups
+    // Pass layout: a lane owns a group (a lane pair when G = 256), EP weights per lane.
+    static constexpr int EP = G <= 128 ? G : 128;
+    static constexpr int KP = G / EP;               // lanes per group in a pass (1 or 2)
+    static constexpr int WP = EP / 2;               // binary16 pairs per lane
+    // Batch layout (INIT, EXACT, EPILOGUE): KB lanes per group, EB weights per lane.
+    static constexpr int EB = G >= 32 ? 32 : 16;
+    static constexpr int KB = G / EB;
+    static constexpr int GB = 64 / KB;              // groups per batch (one tile)
+    static constexpr int WB = EB / 2;
+    static constexpr int NC = G / 8;                // 16-byte chunks per group
+    static constexpr int NS = (G <= 32 ? 2 : 3) * GB;   // staging slots in LDS
     static constexpr int RC = NS <= 64 ? 64 : (NS <= 128 ? 128 : 256);   // ring capacity
-    static constexpr int W = E / 2;                 // packed binary16 pairs per lane
     static constexpr float QMAX = (float)((1 << NBITS) - 1);
     // A binary32 code can disagree with the exact one only if |u - rne(u)| >= kThr.
     static constexpr float kThr = 0.5f - (float)(1.0 / (1 << (24 - NBITS)));
@@ -143,55 +158,61 @@ struct Cfg {
     static constexpr double kElemErr = (double)G / (double)(1 << (24 - NBITS));
 };
 
-// Binary32 evaluation of one lane's E weights at zero z: S = sum|u - q|, Q = sum q,
-// D = max |u - rne(u)| (before any clamp).
-template <int NBITS, int G, bool CLAMP>
-__device__ __forceinline__ void eval_fast(const uint32_t (&xr)[Cfg<NBITS, G>::W], float s, float z,
-                                          float &S, float &Q, float &D)
+// Binary32 evaluation of N binary16 pairs at zero z, for a group whose codes cannot leave
+// [0, 2^NBITS - 1] (the caller checks the group's min and max; clamping groups take the exact
+// path): S = sum|u - q|, T = sum(u - q) and D = max|u - q| with q = rne(u). The code sum
+// follows from T without a sum of its own: sum q = sum u - T, and sum u differs from the
+// exact sum x*s + G*z by at most G half-ulps of u, far below 1/2, so
+// Q = rne(sum x*s + G*z - T) is exact.
+template <int NBITS, int N>
+__device__ __forceinline__ void eval_fast(const uint32_t (&xr)[N], float s, float z, float &S,
+                                          float &T, float &D)
 {
-    using C = Cfg<NBITS, G>;
-    float s0 = 0.f, s1 = 0.f, q0 = 0.f, q1 = 0.f, d0 = 0.f, d1 = 0.f;
+    float s0 = 0.f, s1 = 0.f, t0 = 0.f, t1 = 0.f, d0 = 0.f, d1 = 0.f;
 #pragma unroll
-    for (int i = 0; i < C::W; ++i) {
+    for (int i = 0; i < N; ++i) {
         const float u0 = fmaf(h2f(xr[i] & 0xffffu), s, z);
         const float u1 = fmaf(h2f(xr[i] >> 16), s, z);
-        const float r0 = rintf(u0), r1 = rintf(u1);
-        if (CLAMP) {
-            const float c0 = __builtin_amdgcn_fmed3f(r0, 0.f, C::QMAX);
-            const float c1 = __builtin_amdgcn_fmed3f(r1, 0.f, C::QMAX);
-            s0 += fabsf(u0 - c0);
-            s1 += fabsf(u1 - c1);
-            q0 += c0;
-            q1 += c1;
-        } else {
-            s0 += fabsf(u0 - r0);
-            s1 += fabsf(u1 - r1);
-            q0 += r0;
-            q1 += r1;
-        }
-        d0 = fmaxf(d0, fabsf(u0 - r0));
-        d1 = fmaxf(d1, fabsf(u1 - r1));
+        const float e0 = u0 - rintf(u0), e1 = u1 - rintf(u1);
+        s0 += fabsf(e0);
+        s1 += fabsf(e1);
+        t0 += e0;
+        t1 += e1;
+        d0 = fmaxf(d0, fabsf(e0));
+        d1 = fmaxf(d1, fabsf(e1));
     }
     S = s0 + s1;
-    Q = q0 + q1;
+    T = t0 + t1;
     D = fmaxf(d0, d1);
+    // S and T are read only on some outcomes of the decision; without this the compiler sinks
+    // their sums into those branches and keeps every residual of the lane alive until then.
+    asm volatile("" : "+v"(S), "+v"(T), "+v"(D));
+}
+
+// LDS position (in binary16 elements) of 16-byte chunk c of staging slot j among NS slots:
+// chunk-major, so a lane walks its slot at a constant stride (immediate offsets) and lanes
+// reading the same chunk of different slots touch neighbouring 16-byte words.
+template <int NS>
+__device__ __forceinline__ int chunk_at(int j, int c)
+{
+    return (c * NS + j) << 3;
 }
 
 struct Exact {
     double S, Q, D;
 };
 
-// Exact (binary64) evaluation of one lane's E weights (binary16, in LDS) at zero z. Rare:
-// a rolled loop, so it adds few registers to the binary32 path.
+// Exact (binary64) evaluation of one batch lane's EB weights (chunks c0.. of slot j) at zero
+// z. Rare: a rolled loop, so it adds few registers to the binary32 path.
 template <int NBITS, int G>
-__device__ __forceinline__ Exact eval_exact(const uint16_t *x, float s, float z)
+__device__ __forceinline__ Exact eval_exact(const uint16_t *xs, int j, int c0, float s, float z)
 {
     using C = Cfg<NBITS, G>;
     const double sd = s, zd = z, qm = C::QMAX;
     double s_ = 0.0, q_ = 0.0, d_ = 0.0;
 #pragma unroll 1
-    for (int i = 0; i < C::E; ++i) {
-        const double u = fma((double)h2f(x[i]), sd, zd);
+    for (int i = 0; i < C::EB; ++i) {
+        const double u = fma((double)h2f(xs[chunk_at<C::NS>(j, c0 + (i >> 3)) + (i & 7)]), sd, zd);
         const double c = fmin(fmax(rint(u), 0.0), qm);
         const double e = fabs(u - c);
         s_ += e;
@@ -201,15 +222,42 @@ __device__ __forceinline__ Exact eval_exact(const uint16_t *x, float s, float z)
     return Exact{s_, q_, d_};
 }
 
+// What follows an accepted evaluation (zb, Qb, Db current; sbx: Db is exact): the next zero,
+// the end of the group, or the exact path for a zero update whose shrink may be live.
+enum : uint8_t { kNext = 0, kDone = 1, kNeedShrink = 2 };
+struct Advance {
+    uint8_t out;
+    float zn;
+};
 template <int NBITS, int G>
-__global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
-                                                    const DevJob *__restrict__ jobs)
+__device__ __forceinline__ Advance advance_core(int t, int iters, float s, float zb, float Qb,
+                                                float Db, bool sbx, double X, const float *tau,
+                                                float tau_min)
 {
     using C = Cfg<NBITS, G>;
-    constexpr int E = C::E, K = C::K, GPI = C::GPI, NS = C::NS, W = C::W, RM = C::RC - 1;
+    if (t > iters) return Advance{kDone, zb};
+    // Dead zone of the shrink: max|r| = max|u - q|/s <= beta^(-1/(2-p)), tested with a
+    // relative margin of 4e-6 that covers the binary32 rounding of the products. The
+    // smallest threshold (the last beta) decides most groups at once, for this and every
+    // later iteration.
+    const float dmax = sbx ? Db : Db + (0.5f - C::kThr);
+    const bool dead_all = dmax <= tau_min * s;
+    if (!dead_all && !(dmax <= tau[t - 1] * (s * (1.0f - 4e-6f)))) return Advance{kNeedShrink, zb};
+    const float zn = (float)(((double)Qb - X) * (1.0 / G));
+    if (zn == zb && dead_all) return Advance{kDone, zn};   // exact fixed point
+    return Advance{kNext, zn};
+}
+
+template <int NBITS, int G>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
+{
+    using C = Cfg<NBITS, G>;
+    constexpr int KP = C::KP, WP = C::WP, EB = C::EB, KB = C::KB, GB = C::GB, WB = C::WB;
+    constexpr int NS = C::NS, RM = C::RC - 1;
     static_assert(NS <= 255, "slot indices are bytes");
 
-    // Pool of resident groups: weights and per-group state (one array per field).
+    // Staging slots: weights and per-group state (one array per field).
     __shared__ __attribute__((aligned(16))) uint16_t xs[NS * G];
     __shared__ float st_z[NS];         // candidate zero (next evaluation)
     __shared__ float st_zb[NS];        // accepted zero
@@ -218,22 +266,27 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
     __shared__ float st_Qb[NS];        // accepted sum of codes
     __shared__ float st_Db[NS];        // accepted max |u - q|
     __shared__ double st_Sb[NS];       // accepted sum |u - q|
-    __shared__ double st_sxs[NS];      // exact sum x*s
+    __shared__ double st_X[NS];        // exact sum x*s
     __shared__ uint32_t st_mnmx[NS];   // binary16 min (low half) and max (high half)
     __shared__ uint32_t st_gidx[NS];   // group index within its tensor
     __shared__ uint16_t st_job[NS];    // job index within the launch class
     __shared__ uint8_t st_t[NS];       // index of the next zero update (1-based)
-    __shared__ uint8_t st_fl[NS];      // bit 0: Sb/Db exact; bits 1-2: exact-path work
-    __shared__ uint8_t rings[4 * C::RC];   // slot rings: active, finished, exact-pending, free
-    uint8_t *const ring_act = rings, *const ring_fin = rings + C::RC,
+    __shared__ uint8_t st_fl[NS];      // flags (kSbExact | work << 1 | kFirst)
+    __shared__ uint8_t rings[4 * C::RC];   // slot rings: ready, finished, exact-pending, free
+    uint8_t *const ring_rdy = rings, *const ring_fin = rings + C::RC,
                    *const ring_exq = rings + 2 * C::RC, *const ring_free = rings + 3 * C::RC;
     __shared__ float tau[kMaxIters];
-    __shared__ uint8_t stage[NBITS == 3 ? 64 * E : 4];
+    __shared__ __attribute__((aligned(4))) uint8_t stage[NBITS == 3 ? 64 * EB : 4];
 
     const int lane = threadIdx.x;
-    const int k = lane / K;                      // group within a pass
-    const int sub = lane % K;                    // part of the group
-    const bool leader = sub == 0;
+    // batch layout
+    const int k = lane / KB;                     // group within a batch
+    const int sub = lane % KB;                   // part of the group
+    const bool bleader = sub == 0;
+    // pass layout
+    const int part = lane % KP;
+    const bool pleader = part == 0;
+    const int pbase = lane - part;               // the group's first lane
 
     // Dead-zone thresholds: the shrink of iteration t uses beta_{t-1} = beta0*kappa^(t-1)
     // (binary32 products in order) and maps r to 0 iff |r| <= beta^(-1/(2-p)).
@@ -244,474 +297,638 @@ __global__ void __launch_bounds__(64) stream_kernel(StreamArgs a,
     }
     for (int i = lane; i < NS; i += 64) ring_free[i] = (uint8_t)i;
     __syncthreads();
-    const float tau_min = a.iters > 0 ? tau[a.iters - 1] * (1.0f - 4e-6f) : 0.0f;
+    // wave-uniform: kept in a scalar register
+    const float tau_min = __builtin_bit_cast(
+        float, uniform(__float_as_uint(a.iters > 0 ? tau[a.iters - 1] * (1.0f - 4e-6f) : 0.0f)));
     const double pm1 = (double)a.p - 1.0;
 
-    uint32_t act_h = 0, act_n = 0, fin_h = 0, fin_n = 0, exq_h = 0, exq_n = 0, fre_h = 0, fre_n = NS;
+    uint32_t rdy_h = 0, rdy_n = 0, fin_h = 0, fin_n = 0, exq_h = 0, exq_n = 0, fre_h = 0, fre_n = NS;
 
-    // ---- tile claiming and prefetch -------------------------------------------------------
+    // ---- the lane's group (pass layout) ---------------------------------------------------
+    uint32_t xr[WP];
+#pragma unroll
+    for (int i = 0; i < WP; ++i) xr[i] = 0u;
+    float g_s = 1.f, g_z = 0.f, g_zb = 0.f, g_Qb = 0.f, g_Db = 0.f, g_beta = 0.f;
+    double g_Sb = 0.0, g_X = 0.0;
+    uint32_t g_mnmx = 0, g_gidx = 0, g_job = 0, g_t = 0, g_fl = 0;
+    uint32_t status = kEmpty;
+
+    // ---- tile claiming and prefetch (batch layout) ----------------------------------------
     int64_t tile = 0, tile_end = 0;
     int cur_job = 0;
     bool pf_ok = false;
     int pf_job = 0, pf_nv = 0;
     int64_t pf_g0 = 0;
-    u32x4 pf[E / 8];                             // prefetched weights of the next tile
+    u32x4 pf[EB / 8];                            // prefetched weights of the next tile
 
+    // Claims the next tile and issues its loads. The loads are issued on every call (past the
+    // last tile they re-read the first group of the launch, which is never used), so the
+    // prefetch registers have a single definition in the loop and stay in place: a join
+    // between a loaded and an unloaded version would copy them, and a copy waits for the loads.
     auto prefetch = [&]() {
+        bool ok = true;
         if (tile >= tile_end) {
             uint32_t base = 0;
             if (lane == 0) base = atomic_add_g(a.counter, a.chunk);
             base = uniform(base);
-            if ((int64_t)base >= a.n_tiles) {
-                pf_ok = false;
-#pragma unroll
-                for (int i = 0; i < E / 8; ++i) pf[i] = u32x4{0u, 0u, 0u, 0u};
-                return;
-            }
+            ok = (int64_t)base < a.n_tiles;
             tile = base;
             tile_end = (int64_t)base + a.chunk < a.n_tiles ? (int64_t)base + a.chunk : a.n_tiles;
         }
-        // job of this tile (jobs are ordered by tile0); wave-uniform, so scalar loads
-        while (cur_job + 1 < a.n_jobs && jobs[cur_job + 1].tile0 <= tile)
-            cur_job = (int)uniform((uint32_t)cur_job + 1);
-        while (jobs[cur_job].tile0 > tile) cur_job = (int)uniform((uint32_t)cur_job - 1);
-        const DevJob &J = jobs[cur_job];
-        const int64_t g0 = (tile - J.tile0) * GPI;
-        const int64_t left = J.n_groups - g0;
-        pf_nv = (int)uniform((uint32_t)(left < GPI ? left : GPI));
-        pf_g0 = g0;
-        pf_job = cur_job;
-        // The next tile's weights stay in flight in registers until INIT uses them. Every
-        // lane loads (lanes past a ragged end re-read the tile's first group), so the old
-        // register contents are dead when the loads are issued.
+        const uint16_t *src_w = jobs[0].W;
+        int64_t g0 = 0;
+        if (ok) {
+            // job of this tile (jobs are ordered by tile0); wave-uniform, so scalar loads
+            while (cur_job + 1 < a.n_jobs && jobs[cur_job + 1].tile0 <= tile)
+                cur_job = (int)uniform((uint32_t)cur_job + 1);
+            while (jobs[cur_job].tile0 > tile) cur_job = (int)uniform((uint32_t)cur_job - 1);
+            const DevJob &J = jobs[cur_job];
+            g0 = (tile - J.tile0) * GB;
+            const int64_t left = J.n_groups - g0;
+            pf_nv = (int)uniform((uint32_t)(left < GB ? left : GB));
+            pf_g0 = g0;
+            pf_job = cur_job;
+            src_w = J.W;
+            ++tile;
+        } else {
+            pf_nv = 1;                           // the dummy load reads group 0 of job 0
+        }
+        pf_ok = ok;
+        // Every lane loads (lanes past a ragged end re-read the tile's first group). The loads
+        // stay below the last use of the previous tile's registers, so the two share registers.
+        __builtin_amdgcn_sched_barrier(0);
         const int64_t gl = g0 + (k < pf_nv ? k : 0);
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(J.W + gl * G + sub * E);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(src_w + gl * G + sub * EB);
 #pragma unroll
-        for (int i = 0; i < E / 8; ++i) pf[i] = gbl(const_cast<u32x4 *>(src))[i];
-        pf_ok = true;
-        ++tile;
+        for (int i = 0; i < EB / 8; ++i) pf[i] = gbl(const_cast<u32x4 *>(src))[i];
     };
 
-    // ---- queue pushes (one entry per group, by its leader lane) -------------------------
-    auto push = [&](bool valid, uint8_t out, uint8_t slot) {
-        const uint64_t m_act = __ballot(valid && leader && out == kActive);
-        const uint64_t m_fin = __ballot(valid && leader && out == kFinished);
-        const uint64_t m_exq = __ballot(valid && leader && out == kExact);
-        if (valid && leader) {
-            if (out == kActive) ring_act[(act_h + act_n + lanes_below(m_act)) & RM] = slot;
-            else if (out == kFinished) ring_fin[(fin_h + fin_n + lanes_below(m_fin)) & RM] = slot;
-            else ring_exq[(exq_h + exq_n + lanes_below(m_exq)) & RM] = slot;
+    // Rank of this lane's group among the groups whose leading lane is set in m.
+    auto group_rank = [&](uint64_t m, int first_lane) -> uint32_t {
+        return (uint32_t)lanes_below(m & ~(1ull << first_lane));
+    };
+
+    // Pushes slot j of each batch group onto the ring its outcome names (leaders only).
+    auto push_batch = [&](bool valid, uint8_t out, uint8_t j) {
+        const uint64_t m_rdy = __ballot(valid && bleader && out == kNext);
+        const uint64_t m_fin = __ballot(valid && bleader && out == kDone);
+        const uint64_t m_exq = __ballot(valid && bleader && out == kNeedShrink);
+        if (valid && bleader) {
+            if (out == kNext) ring_rdy[(rdy_h + rdy_n + lanes_below(m_rdy)) & RM] = j;
+            else if (out == kDone) ring_fin[(fin_h + fin_n + lanes_below(m_fin)) & RM] = j;
+            else ring_exq[(exq_h + exq_n + lanes_below(m_exq)) & RM] = j;
         }
-        act_n += (uint32_t)__builtin_popcountll(m_act);
+        rdy_n += (uint32_t)__builtin_popcountll(m_rdy);
         fin_n += (uint32_t)__builtin_popcountll(m_fin);
         exq_n += (uint32_t)__builtin_popcountll(m_exq);
     };
 
-    // ---- after an accepted evaluation (zb, Qb, Db, sbx already current in registers):
-    //      the next zero, or finished / exact path. Writes the fields it changes.
-    auto advance = [&](uint8_t slot, float s, float zb, float Qb, float Db, bool sbx) -> uint8_t {
-        const int t = st_t[slot];
-        if (t > a.iters) return kFinished;
-        // Dead zone of the shrink: max|r| = max|u - q|/s <= beta^(-1/(2-p)), tested with a
-        // relative margin of 4e-6 that covers the binary32 rounding of the products. The
-        // smallest threshold (the last beta) decides most groups at once, for this and every
-        // later iteration.
-        const float dmax = sbx ? Db : Db + (0.5f - C::kThr);
-        const bool dead_all = dmax <= tau_min * s;
-        if (!dead_all && !(dmax <= tau[t - 1] * (s * (1.0f - 4e-6f)))) {
-            if (leader) st_fl[slot] = (uint8_t)((sbx ? 1 : 0) | (kShrink << 1));
-            return kExact;                           // the shrink may move residuals
+    // Batch version of the advance step, on slot j (fields written by the group's leader).
+    auto advance_slot = [&](uint8_t j, float s, float zb, float Qb, float Db, bool sbx) -> uint8_t {
+        const int t = st_t[j];
+        const Advance ad = advance_core<NBITS, G>(t, a.iters, s, zb, Qb, Db, sbx, st_X[j], tau,
+                                                  tau_min);
+        if (bleader) {
+            if (ad.out == kDone) st_zb[j] = ad.zn;
+            else if (ad.out == kNeedShrink) st_fl[j] = (uint8_t)((sbx ? kSbExact : 0) | (kShrink << 1));
+            else {
+                st_z[j] = ad.zn;
+                st_beta[j] = st_beta[j] * a.kappa;
+                st_t[j] = (uint8_t)(t + 1);
+            }
         }
-        const float zn = (float)(((double)Qb - st_sxs[slot]) * (1.0 / G));
-        if (zn == zb && dead_all) {                  // exact fixed point
-            if (leader) st_zb[slot] = zn;
-            return kFinished;
-        }
-        if (leader) {
-            st_z[slot] = zn;
-            st_beta[slot] = st_beta[slot] * a.kappa;
-            st_t[slot] = (uint8_t)(t + 1);
-        }
-        return kActive;
+        return ad.out;
     };
 
-    int mm_job = -1;                             // running zero (min, max) of one tensor
+    // Solver state of a group in a slot (read by every lane of the group, written by its
+    // first lane) and in the lane's registers.
+    struct GroupState {
+        float s, z, zb, Qb, Db, beta;
+        double Sb, X;
+        uint32_t mnmx, gidx, job, t, fl;
+    };
+    auto load_state = [&](int j) -> GroupState {
+        return GroupState{st_s[j], st_z[j], st_zb[j], st_Qb[j], st_Db[j], st_beta[j], st_Sb[j],
+                          st_X[j], st_mnmx[j], st_gidx[j], st_job[j], st_t[j], st_fl[j]};
+    };
+    auto save_state = [&](int j) {
+        st_s[j] = g_s;
+        st_z[j] = g_z;
+        st_zb[j] = g_zb;
+        st_Qb[j] = g_Qb;
+        st_Db[j] = g_Db;
+        st_beta[j] = g_beta;
+        st_Sb[j] = g_Sb;
+        st_X[j] = g_X;
+        st_mnmx[j] = g_mnmx;
+        st_gidx[j] = g_gidx;
+        st_job[j] = (uint16_t)g_job;
+        st_t[j] = (uint8_t)g_t;
+        st_fl[j] = (uint8_t)g_fl;
+    };
+    auto set_state = [&](const GroupState &n) {
+        g_s = n.s;
+        g_z = n.z;
+        g_zb = n.zb;
+        g_Qb = n.Qb;
+        g_Db = n.Db;
+        g_beta = n.beta;
+        g_Sb = n.Sb;
+        g_X = n.X;
+        g_mnmx = n.mnmx;
+        g_gidx = n.gidx;
+        g_job = n.job;
+        g_t = n.t;
+        g_fl = n.fl;
+    };
+
+    // Per-tensor (min, max) of the binary32 zeros for the 8-bit requantization: a running pair
+    // per lane for the tensor the wave's batches currently belong to, reduced over the wave and
+    // flushed with atomics only when that tensor changes (all waves work on the same tensors
+    // at once, so atomics per batch would serialise).
+    int mm_job = -1;
     float mm_lo = INFINITY, mm_hi = -INFINITY;
     auto flush_minmax = [&]() {
-        if (mm_job >= 0 && lane == 0) {
-            atomic_min_g(jobs[mm_job].minmax, fkey(mm_lo));
-            atomic_max_g(jobs[mm_job].minmax + 1, fkey(mm_hi));
+        if (mm_job >= 0) {
+            const float lo = minf_k<64>(mm_lo), hi = maxf_k<64>(mm_hi);
+            if (lane == 0) {
+                atomic_min_g(jobs[mm_job].minmax, fkey(lo));
+                atomic_max_g(jobs[mm_job].minmax + 1, fkey(hi));
+            }
         }
+        mm_lo = INFINITY;
+        mm_hi = -INFINITY;
     };
+
+    // ================= EPILOGUE: codes, packing, scale / zero of up to GB finished groups
+    auto epilogue = [&]() {
+        // One tensor per batch (descriptor in scalar registers); groups of another tensor
+        // go back to the finished list for a later batch.
+        const int n = fin_n < GB ? (int)fin_n : GB;
+        bool valid = k < n;
+        uint8_t j = 0;
+        if (valid) j = ring_fin[(fin_h + k) & RM];
+        fin_h = (fin_h + n) & RM;
+        fin_n -= n;
+        uint32_t job = 0;
+        if (valid) job = st_job[j];
+        const uint32_t job0 = uniform(job);      // lane 0 always holds a group
+        const bool later = valid && job != job0;
+        const uint64_t m_later = __ballot(later && bleader);
+        if (later && bleader) ring_fin[(fin_h + fin_n + lanes_below(m_later)) & RM] = j;
+        fin_n += (uint32_t)__builtin_popcountll(m_later);
+        valid = valid && !later;
+        const DevJob &J = jobs[job0];
+        float zb = 0.f;
+        uint32_t gidx = 0;
+        if (valid) {
+            zb = st_zb[j];
+            const float s = st_s[j];
+            gidx = st_gidx[j];
+            const int64_t e0 = (int64_t)gidx * G + sub * EB;   // first weight of this lane
+            // Packs this lane's EB codes and stores them. v[i] is either the exact code
+            // or a u whose code is rne(u) in [0, 2^NBITS - 1]: v_cvt_pk_u8_f32 rounds
+            // half to even and saturates to [0, 255], so either way it yields the code.
+            auto emit = [&](const float (&v)[EB]) {
+                // bytes of codes, then NBITS-bit fields: byte b of plane m holds code
+                // PL*b + m, so plane m shifts by NBITS*m (3-bit codes: one per byte)
+                constexpr int PL = NBITS == 3 ? 1 : 8 / NBITS;   // planes
+                constexpr int BY = EB / PL < 4 ? EB / PL : 4;    // bytes per word
+                constexpr int PER = BY * PL;           // codes per word
+                constexpr int NW = EB / PER;
+                uint32_t w[NW];
+#pragma unroll
+                for (int q = 0; q < NW; ++q) {
+                    uint32_t pl[PL];
+#pragma unroll
+                    for (int m = 0; m < PL; ++m) {
+                        uint32_t acc = 0;
+#pragma unroll
+                        for (int b = 0; b < BY; ++b)
+                            acc = __builtin_amdgcn_cvt_pk_u8_f32(v[PER * q + PL * b + m], b, acc);
+                        pl[m] = acc;
+                    }
+                    uint32_t word = pl[0];
+#pragma unroll
+                    for (int m = 1; m < PL; ++m) word |= pl[m] << (NBITS * m);
+                    w[q] = word;
+                }
+                if constexpr (NBITS == 3) {
+                    // one code per byte into the stage; words are formed below
+#pragma unroll
+                    for (int q = 0; q < NW; ++q)
+                        *reinterpret_cast<uint32_t *>(stage + lane * EB + 4 * q) = w[q];
+                } else {
+                    uint8_t *dst = J.packed + e0 * NBITS / 8;
+                    if constexpr (BY == 2)             // 16 one-bit codes
+                        *gbl(reinterpret_cast<uint16_t *>(dst)) = (uint16_t)w[0];
+                    else if constexpr (NW == 4)
+                        *gbl(reinterpret_cast<u32x4 *>(dst)) = u32x4{w[0], w[1], w[2], w[3]};
+                    else if constexpr (NW == 2)
+                        *gbl(reinterpret_cast<u32x2 *>(dst)) = u32x2{w[0], w[1]};
+                    else if constexpr (NW == 1)
+                        *gbl(reinterpret_cast<uint32_t *>(dst)) = w[0];
+                    else {
+#pragma unroll
+                        for (int q = 0; q < NW / 4; ++q)
+                            gbl(reinterpret_cast<u32x4 *>(dst))[q] =
+                                u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+                    }
+                }
+            };
+            // The accepted evaluation ran in binary32 with the same operations (so its D
+            // bounds these codes: none is next to a rounding boundary and none clamps)
+            // or in binary64; exact codes only if D was near 1/2. Each branch packs its
+            // own values, so they cross no join.
+            if (st_Db[j] < C::kThr - (float)(1.0 / (1 << (24 - NBITS)))) {
+                float u[EB];
+#pragma unroll
+                for (int c = 0; c < EB / 8; ++c) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::NS>(j, sub * (EB / 8) + c));
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t h = i & 1 ? w4[i >> 1] >> 16 : w4[i >> 1] & 0xffffu;
+                        u[8 * c + i] = fmaf(h2f(h), s, zb);
+                    }
+                }
+                emit(u);
+            } else {
+                float code[EB];
+#pragma unroll 1
+                for (int i = 0; i < EB; ++i) {
+                    const int c = sub * (EB / 8) + (i >> 3);
+                    const double u = fma((double)h2f(xs[chunk_at<C::NS>(j, c) + (i & 7)]), (double)s, (double)zb);
+                    const float cf = (float)fmin(fmax(rint(u), 0.0), (double)C::QMAX);
+#pragma unroll
+                    for (int m = 0; m < EB; ++m)
+                        if (m == i) code[m] = cf;
+                }
+                emit(code);
+            }
+            if (bleader) {
+                gbl(J.scale)[gidx] = f2h(1.0f / s);
+                if (J.zero16) gbl(J.zero16)[gidx] = f2h(zb);
+                if (J.zero32) gbl(J.zero32)[gidx] = zb;
+                // evaluations run = index of the next update when the group stops
+                if (J.passes) gbl(J.passes)[gidx] = st_t[j];
+            }
+        }
+        if constexpr (NBITS == 3) {
+            // Flat 10-code words: words wholly inside the group are written here; a word
+            // shared with a neighbouring group goes to the stash (joined after the solve).
+            __syncthreads();
+            if (valid) {
+                const int64_t c0 = (int64_t)gidx * G;          // first code of the group
+                const int64_t c1 = c0 + G;                      // one past the last
+                const int64_t ncode = J.n_groups * G;
+                const int64_t w0 = c0 / 10, w1 = (c1 - 1) / 10;
+                auto out = gbl(reinterpret_cast<uint32_t *>(J.packed));
+                for (int64_t w = w0 + sub; w <= w1; w += KB) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int c = 0; c < 10; ++c) {
+                        const int64_t ci = w * 10 + c;
+                        if (ci >= c0 && ci < c1)
+                            word |= (uint32_t)stage[k * G + (int)(ci - c0)] << (3 * c);
+                    }
+                    const bool head = w * 10 < c0;                  // shared with group-1
+                    const bool tail = w * 10 + 10 > c1 && c1 < ncode; // shared with group+1
+                    uint32_t *st2 = reinterpret_cast<uint32_t *>(J.stash + gidx);
+                    if (head) gbl(st2)[1] = word;
+                    else if (tail) gbl(st2)[0] = word;
+                    else out[w] = word;
+                }
+            }
+            __syncthreads();
+        }
+        if (J.minmax) {
+            if ((int)job0 != mm_job) {
+                flush_minmax();
+                mm_job = (int)job0;
+            }
+            if (valid) {
+                mm_lo = fminf(mm_lo, zb);
+                mm_hi = fmaxf(mm_hi, zb);
+            }
+        }
+        const uint64_t m_done = __ballot(valid && bleader);
+        if (valid && bleader) ring_free[(fre_h + fre_n + lanes_below(m_done)) & RM] = j;
+        fre_n += (uint32_t)__builtin_popcountll(m_done);
+    };
+
+    // A bound on loop steps that the schedule never reaches (every step moves at least one
+    // group forward): a defect would end the launch instead of hanging it.
+    int64_t budget = 1024;
 
     prefetch();
 
-    while (true) {
-        if (pf_ok && act_n < GPI && fre_n >= GPI) {
-            // ================= INIT: a prefetched tile enters the pool =================
-            const int nv = pf_nv;
-            const bool valid = k < nv;
-            uint8_t slot = 0;
-            if (valid) slot = ring_free[(fre_h + k) & RM];
-            fre_h = (fre_h + nv) & RM;
-            fre_n -= nv;
-            uint8_t out = kFinished;
-            if (valid) {
-                uint32_t xr[W];
-                u32x4 *dst = reinterpret_cast<u32x4 *>(xs + slot * G + sub * E);
-#pragma unroll
-                for (int i = 0; i < E / 8; ++i) {
-                    const u32x4 v = pf[i];
-                    dst[i] = v;
-                    xr[4 * i] = v.x;
-                    xr[4 * i + 1] = v.y;
-                    xr[4 * i + 2] = v.z;
-                    xr[4 * i + 3] = v.w;
-                }
-                // min / max on binary16 pairs, then across the group
-                h2v hmn = __builtin_bit_cast(h2v, xr[0]), hmx = hmn;
-#pragma unroll
-                for (int i = 1; i < W; ++i) {
-                    const h2v h = __builtin_bit_cast(h2v, xr[i]);
-                    hmn = __builtin_elementwise_min(hmn, h);
-                    hmx = __builtin_elementwise_max(hmx, h);
-                }
-                float mn = fminf((float)hmn.x, (float)hmn.y);
-                float mx = fmaxf((float)hmx.x, (float)hmx.y);
-                mn = minf_k<K>(mn);
-                mx = maxf_k<K>(mx);
-                const float rng = mx - mn;
-                const float s = rng > 0.0f ? C::QMAX / rng : 1.0f;
-                const float z0 = 0.0f - mn * s;      // +0 when min is a zero of either sign
-                const double sd = s;
-                double sxs = 0.0;
-#pragma unroll
-                for (int i = 0; i < 2 * W; ++i)
-                    sxs = fma((double)h2f(i & 1 ? xr[i >> 1] >> 16 : xr[i >> 1] & 0xffffu), sd, sxs);
-                sxs = addd_k<K>(sxs);
-                float S, Q, D;
-                eval_fast<NBITS, G, false>(xr, s, z0, S, Q, D);
-                S = addf_k<K>(S);
-                Q = addf_k<K>(Q);
-                D = maxf_k<K>(D);
-                double Sb = S;
-                bool sbx = false;
-                if (D >= C::kThr) {                  // a code may differ from the exact one
-                    const Exact x0 = eval_exact<NBITS, G>(xs + slot * G + sub * E, s, z0);
-                    Sb = addd_k<K>(x0.S);
-                    Q = (float)addd_k<K>(x0.Q);
-                    D = (float)maxf_k<K>((float)x0.D);
-                    sbx = true;
-                }
-                if (leader) {
-                    st_z[slot] = z0;
-                    st_zb[slot] = z0;
-                    st_s[slot] = s;
-                    st_beta[slot] = a.beta0;
-                    st_Qb[slot] = Q;
-                    st_Db[slot] = D;
-                    st_Sb[slot] = Sb;
-                    st_sxs[slot] = sxs;
-                    st_mnmx[slot] = (uint32_t)f2h(mn) | ((uint32_t)f2h(mx) << 16);
-                    st_gidx[slot] = (uint32_t)(pf_g0 + k);
-                    st_job[slot] = (uint16_t)pf_job;
-                    st_t[slot] = 1;
-                    st_fl[slot] = sbx ? 1 : 0;
-                }
-                out = advance(slot, s, z0, Q, D, sbx);
+    // The outer loop takes one prefetched tile in per turn (INIT); the inner loop does all
+    // other work. Only the outer loop touches the prefetch registers, so they keep one place.
+    bool done = false;
+    while (!done) {
+        while (true) {
+            if (--budget <= 0) {
+                done = true;
+                break;
             }
-            push(valid, out, slot);
-            prefetch();
-            continue;
-        }
+            const bool lead = pleader;
+            const bool holder = status == kHoldFin || status == kHoldExq;
+            const uint64_t m_hold = __ballot(holder && lead);
+            const uint64_t m_empty = __ballot(status == kEmpty && lead);
+            const uint32_t n_hold = (uint32_t)__builtin_popcountll(m_hold);
+            const uint32_t n_empty = (uint32_t)__builtin_popcountll(m_empty);
 
-        if (fin_n >= GPI || (fin_n > 0 && act_n < GPI && (fre_n < GPI || !pf_ok))) {
-            // ================= EPILOGUE: codes, packing, scale / zero ===================
-            // One tensor per batch (descriptor in scalar registers); groups of another tensor
-            // go back to the finished list for a later batch.
-            const int n = fin_n < GPI ? (int)fin_n : GPI;
-            bool valid = k < n;
-            uint8_t slot = 0;
-            if (valid) slot = ring_fin[(fin_h + k) & RM];
-            fin_h = (fin_h + n) & RM;
-            fin_n -= n;
-            uint32_t job = 0;
-            if (valid) job = st_job[slot];
-            const uint32_t job0 = uniform(job);      // lane 0 always holds a group
-            const bool later = valid && job != job0;
-            const uint64_t m_later = __ballot(later && leader);
-            if (later && leader) ring_fin[(fin_h + fin_n + lanes_below(m_later)) & RM] = slot;
-            fin_n += (uint32_t)__builtin_popcountll(m_later);
-            valid = valid && !later;
-            const DevJob &J = jobs[job0];
-            float zb = 0.f;
-            uint32_t code[E];
-            uint32_t gidx = 0;
-            if (valid) {
-                zb = st_zb[slot];
-                const float s = st_s[slot];
-                gidx = st_gidx[slot];
-                const uint16_t *xl = xs + slot * G + sub * E;
-                uint32_t xr[W];
+            // A tile comes in first when the ready groups cannot fill the lanes about to need
+            // one and the slots stay enough for every holder: one swap then serves them all.
+            if (pf_ok && rdy_n < n_empty + n_hold && fre_n >= GB + n_hold) break;   // INIT
+
+            if ((n_hold > 0 && (rdy_n > 0 || fre_n > 0)) || (n_empty > 0 && rdy_n > 0)) {
+                // ================= SWAP: groups leave lanes for slots and enter from slots ====
+                // Holders store their group in a free slot; lanes left without a group load a
+                // ready one. Only when no slot is free does a holder exchange its group with a
+                // ready one in place (chunk by chunk, read before write).
+                const uint32_t n_out = n_hold < fre_n ? n_hold : fre_n;
+                const uint32_t n_x = n_out < n_hold ? (n_hold - n_out < rdy_n ? n_hold - n_out : rdy_n) : 0;
+                const uint32_t rk_h = group_rank(m_hold, pbase);
+                const bool out_l = holder && rk_h < n_out;
+                const bool exch_l = holder && rk_h >= n_out && rk_h - n_out < n_x;
+                const bool no_group = status == kEmpty || out_l;
+                const uint64_t m_ng = __ballot(no_group && lead);
+                const uint32_t n_ng = (uint32_t)__builtin_popcountll(m_ng);
+                const uint32_t n_in = n_ng < rdy_n - n_x ? n_ng : rdy_n - n_x;
+                const uint32_t rk_n = group_rank(m_ng, pbase);
+                const bool in_l = no_group && rk_n < n_in;
+                int jo = -1, ji = -1;
+                if (out_l) jo = ring_free[(fre_h + rk_h) & RM];
+                if (exch_l) jo = ring_rdy[(rdy_h + rk_h - n_out) & RM];
+                if (in_l) ji = ring_rdy[(rdy_h + n_x + rk_n) & RM];
+                if (n_x > 0 && exch_l) {
 #pragma unroll
-                for (int i = 0; i < E / 8; ++i) {
-                    const uint4 v = reinterpret_cast<const uint4 *>(xl)[i];
-                    xr[4 * i] = v.x;
-                    xr[4 * i + 1] = v.y;
-                    xr[4 * i + 2] = v.z;
-                    xr[4 * i + 3] = v.w;
-                }
-                uint32_t near = 0;                   // codes next to a rounding boundary
-#pragma unroll
-                for (int i = 0; i < E; ++i) {
-                    const uint32_t h = i & 1 ? xr[i >> 1] >> 16 : xr[i >> 1] & 0xffffu;
-                    const float u = fmaf(h2f(h), s, zb);
-                    const float r = rintf(u);
-                    near |= (fabsf(u - r) >= C::kThr ? 1u : 0u) << i;
-                    code[i] = (uint32_t)__builtin_amdgcn_fmed3f(r, 0.f, C::QMAX);
-                }
-                if (near) {                          // exact codes there (binary64)
-#pragma unroll 1
-                    for (int i = 0; i < E; ++i) {
-                        if (near >> i & 1u) {
-                            const double u = fma((double)h2f(xl[i]), (double)s, (double)zb);
-                            const uint32_t c = (uint32_t)fmin(fmax(rint(u), 0.0), (double)C::QMAX);
-#pragma unroll
-                            for (int j = 0; j < E; ++j)
-                                if (j == i) code[j] = c;
-                        }
+                    for (int c = 0; c < WP / 4; ++c) {
+                        u32x4 *q = reinterpret_cast<u32x4 *>(xs + chunk_at<C::NS>(jo, part * (WP / 4) + c));
+                        const u32x4 v = *q;
+                        *q = u32x4{xr[4 * c], xr[4 * c + 1], xr[4 * c + 2], xr[4 * c + 3]};
+                        xr[4 * c] = v.x;
+                        xr[4 * c + 1] = v.y;
+                        xr[4 * c + 2] = v.z;
+                        xr[4 * c + 3] = v.w;
                     }
+                    const GroupState ns = load_state(jo);
+                    if (lead) save_state(jo);
+                    set_state(ns);
                 }
-                const int64_t e0 = (int64_t)gidx * G + sub * E;   // first weight of this lane
-                if constexpr (NBITS == 8) {
-                    auto dst = gbl(reinterpret_cast<u32x4 *>(J.packed + e0));
+                if (out_l) {
 #pragma unroll
-                    for (int i = 0; i < E / 16; ++i) {
-                        u32x4 o;
-                        o.x = code[16 * i] | code[16 * i + 1] << 8 | code[16 * i + 2] << 16 | code[16 * i + 3] << 24;
-                        o.y = code[16 * i + 4] | code[16 * i + 5] << 8 | code[16 * i + 6] << 16 | code[16 * i + 7] << 24;
-                        o.z = code[16 * i + 8] | code[16 * i + 9] << 8 | code[16 * i + 10] << 16 | code[16 * i + 11] << 24;
-                        o.w = code[16 * i + 12] | code[16 * i + 13] << 8 | code[16 * i + 14] << 16 | code[16 * i + 15] << 24;
-                        dst[i] = o;
+                    for (int c = 0; c < WP / 4; ++c)
+                        *reinterpret_cast<u32x4 *>(xs + chunk_at<C::NS>(jo, part * (WP / 4) + c)) =
+                            u32x4{xr[4 * c], xr[4 * c + 1], xr[4 * c + 2], xr[4 * c + 3]};
+                    if (lead) save_state(jo);
+                }
+                if (in_l) {
+#pragma unroll
+                    for (int c = 0; c < WP / 4; ++c) {
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::NS>(ji, part * (WP / 4) + c));
+                        xr[4 * c] = v.x;
+                        xr[4 * c + 1] = v.y;
+                        xr[4 * c + 2] = v.z;
+                        xr[4 * c + 3] = v.w;
                     }
-                } else if constexpr (NBITS == 4 || NBITS == 2 || NBITS == 1) {
-                    constexpr int PER = 32 / NBITS;       // codes per 32-bit word
-                    constexpr int NW = E / PER > 0 ? E / PER : 1;
-                    uint32_t w[NW];
-#pragma unroll
-                    for (int i = 0; i < NW; ++i) w[i] = 0;
-#pragma unroll
-                    for (int i = 0; i < E; ++i) w[i / PER] |= code[i] << (NBITS * (i % PER));
-                    uint8_t *dst = J.packed + e0 * NBITS / 8;
-                    if constexpr (E * NBITS == 128)
-                        *gbl(reinterpret_cast<u32x4 *>(dst)) = u32x4{w[0], w[1], w[2], w[3]};
-                    else if constexpr (E * NBITS == 64)
-                        *gbl(reinterpret_cast<u32x2 *>(dst)) = u32x2{w[0], w[1]};
-                    else if constexpr (E * NBITS == 32)
-                        *gbl(reinterpret_cast<uint32_t *>(dst)) = w[0];
-                    else
-                        *gbl(reinterpret_cast<uint16_t *>(dst)) = (uint16_t)w[0];
+                    set_state(load_state(ji));
                 }
-                if (leader) {
-                    gbl(J.scale)[gidx] = f2h(1.0f / s);
-                    if (J.zero16) gbl(J.zero16)[gidx] = f2h(zb);
-                    if (J.zero32) gbl(J.zero32)[gidx] = zb;
-                    // evaluations run = index of the next update when the group stops
-                    if (J.passes) gbl(J.passes)[gidx] = st_t[slot];
+                // rings: stored groups go to finished / exact-pending; the slots of loaded
+                // groups become free
+                const bool stored = out_l || exch_l;
+                const bool to_fin = stored && status == kHoldFin;
+                const uint64_t m_f = __ballot(to_fin && lead);
+                const uint64_t m_x = __ballot(stored && !to_fin && lead);
+                const uint64_t m_fr = __ballot(in_l && lead);
+                if (stored && lead) {
+                    if (to_fin) ring_fin[(fin_h + fin_n + lanes_below(m_f)) & RM] = (uint8_t)jo;
+                    else ring_exq[(exq_h + exq_n + lanes_below(m_x)) & RM] = (uint8_t)jo;
                 }
-                if constexpr (NBITS == 3) {
-#pragma unroll
-                    for (int i = 0; i < E; ++i) stage[lane * E + i] = (uint8_t)code[i];
-                }
+                rdy_h = (rdy_h + n_x + n_in) & RM;
+                rdy_n -= n_x + n_in;
+                fre_h = (fre_h + n_out) & RM;
+                fre_n -= n_out;
+                if (in_l && lead) ring_free[(fre_h + fre_n + lanes_below(m_fr)) & RM] = (uint8_t)ji;
+                fre_n += (uint32_t)__builtin_popcountll(m_fr);
+                fin_n += (uint32_t)__builtin_popcountll(m_f);
+                exq_n += (uint32_t)__builtin_popcountll(m_x);
+                if (in_l || exch_l) status = kActive;
+                else if (out_l) status = kEmpty;
+                continue;
             }
-            if constexpr (NBITS == 3) {
-                // Flat 10-code words: words wholly inside the group are written here; a word
-                // shared with a neighbouring group goes to the stash (joined after the solve).
-                __syncthreads();
+
+            const uint32_t n_act = (uint32_t)__builtin_popcountll(__ballot(status == kActive && lead));
+            const bool can_init = pf_ok && fre_n >= GB;
+            const bool idle = n_act == 0;            // no pass possible now
+
+            if (fin_n >= GB || (fin_n > 0 && idle && !can_init && rdy_n == 0 && exq_n == 0)) {
+                epilogue();
+                continue;
+            }
+
+            if (exq_n >= GB || (exq_n > 0 && idle && rdy_n == 0)) {
+                // ================= EXACT: binary64 decisions and shrink updates ==============
+                const int n = exq_n < GB ? (int)exq_n : GB;
+                const bool valid = k < n;
+                uint8_t j = 0;
+                if (valid) j = ring_exq[(exq_h + k) & RM];
+                exq_h = (exq_h + n) & RM;
+                exq_n -= n;
+                uint8_t out = kDone;
                 if (valid) {
-                    const int64_t c0 = (int64_t)gidx * G;          // first code of the group
-                    const int64_t c1 = c0 + G;                      // one past the last
-                    const int64_t ncode = J.n_groups * G;
-                    const int64_t w0 = c0 / 10, w1 = (c1 - 1) / 10;
-                    auto out = gbl(reinterpret_cast<uint32_t *>(J.packed));
-                    for (int64_t w = w0 + sub; w <= w1; w += K) {
-                        uint32_t word = 0;
-#pragma unroll
-                        for (int c = 0; c < 10; ++c) {
-                            const int64_t ci = w * 10 + c;
-                            if (ci >= c0 && ci < c1)
-                                word |= (uint32_t)stage[k * G + (int)(ci - c0)] << (3 * c);
+                    const float s = st_s[j];
+                    const uint8_t fl = st_fl[j];
+                    const int c0 = sub * (EB / 8);
+                    if (((fl >> 1) & 3) == kDecide) {
+                        const float z = st_z[j];
+                        const Exact xn = eval_exact<NBITS, G>(xs, j, c0, s, z);
+                        const double S = addd_k<KB>(xn.S);
+                        const float Q = (float)addd_k<KB>(xn.Q);
+                        const float D = maxf_k<KB>((float)xn.D);
+                        double Sb = st_Sb[j];
+                        if (!(fl & kFirst) && !(fl & kSbExact))
+                            Sb = addd_k<KB>(eval_exact<NBITS, G>(xs, j, c0, s, st_zb[j]).S);
+                        if ((fl & kFirst) || !a.early_stop || S <= Sb) {
+                            if (bleader) {
+                                st_zb[j] = z;
+                                st_Sb[j] = S;
+                                st_Qb[j] = Q;
+                                st_Db[j] = D;
+                                st_fl[j] = kSbExact;
+                            }
+                            out = advance_slot(j, s, z, Q, D, true);
+                        } else {
+                            out = kDone;
                         }
-                        const bool head = w * 10 < c0;                  // shared with group-1
-                        const bool tail = w * 10 + 10 > c1 && c1 < ncode; // shared with group+1
-                        uint32_t *st2 = reinterpret_cast<uint32_t *>(J.stash + gidx);
-                        if (head) gbl(st2)[1] = word;
-                        else if (tail) gbl(st2)[0] = word;
-                        else out[w] = word;
-                    }
-                }
-                __syncthreads();
-            }
-            // Per-tensor (min, max) of the binary32 zeros for the 8-bit requantization: a
-            // running pair per wave, flushed with atomics only when the tensor changes (all
-            // waves work on the same tensor at once, so per-batch atomics would serialise).
-            if (J.minmax) {
-                float lo = valid ? zb : INFINITY, hi = valid ? zb : -INFINITY;
-                lo = __builtin_bit_cast(float, uniform(__float_as_uint(minf_k<64>(lo))));
-                hi = __builtin_bit_cast(float, uniform(__float_as_uint(maxf_k<64>(hi))));
-                if ((int)job0 != mm_job) {
-                    flush_minmax();
-                    mm_job = (int)job0;
-                    mm_lo = lo;
-                    mm_hi = hi;
-                } else {
-                    mm_lo = fminf(mm_lo, lo);
-                    mm_hi = fmaxf(mm_hi, hi);
-                }
-            }
-            const uint64_t m_done = __ballot(valid && leader);
-            if (valid && leader) ring_free[(fre_h + fre_n + lanes_below(m_done)) & RM] = slot;
-            fre_n += (uint32_t)__builtin_popcountll(m_done);
-            continue;
-        }
-
-        if (exq_n >= GPI || (exq_n > 0 && act_n < GPI && (fre_n < GPI || !pf_ok))) {
-            // ================= EXACT: binary64 decisions and shrink updates ==============
-            const int n = exq_n < GPI ? (int)exq_n : GPI;
-            const bool valid = k < n;
-            uint8_t slot = 0;
-            if (valid) slot = ring_exq[(exq_h + k) & RM];
-            exq_h = (exq_h + n) & RM;
-            exq_n -= n;
-            uint8_t out = kFinished;
-            if (valid) {
-                const uint16_t *xl = xs + slot * G + sub * E;
-                const float s = st_s[slot];
-                const uint8_t fl = st_fl[slot];
-                if ((fl >> 1) == kDecide) {
-                    const float z = st_z[slot];
-                    const Exact xn = eval_exact<NBITS, G>(xl, s, z);
-                    const double S = addd_k<K>(xn.S);
-                    const float Q = (float)addd_k<K>(xn.Q);
-                    const float D = maxf_k<K>((float)xn.D);
-                    double Sb = st_Sb[slot];
-                    if (!(fl & 1)) Sb = addd_k<K>(eval_exact<NBITS, G>(xl, s, st_zb[slot]).S);
-                    if (!a.early_stop || S <= Sb) {
-                        if (leader) {
-                            st_zb[slot] = z;
-                            st_Sb[slot] = S;
-                            st_Qb[slot] = Q;
-                            st_Db[slot] = D;
-                            st_fl[slot] = 1;
-                        }
-                        out = advance(slot, s, z, Q, D, true);
                     } else {
-                        out = kFinished;
-                    }
-                } else {
-                    // zero update with the shrink live: z = mean(q - (x - W_e)*s), W_e from
-                    // the residual r = x - W_r = (u - q)/s of the accepted iterate.
-                    const double sd = s, zd = st_zb[slot], qm = C::QMAX;
-                    const double beta = st_beta[slot];
-                    double acc = 0.0;
+                        // zero update with the shrink live: z = mean(q - (x - W_e)*s), W_e from
+                        // the residual r = x - W_r = (u - q)/s of the accepted iterate.
+                        const double sd = s, zd = st_zb[j], qm = C::QMAX;
+                        const double beta = st_beta[j];
+                        double acc = 0.0;
 #pragma unroll 1
-                    for (int i = 0; i < E; ++i) {
-                        const double xv = h2f(xl[i]);
-                        const double u = fma(xv, sd, zd);
-                        const double c = fmin(fmax(rint(u), 0.0), qm);
-                        const double we = shrink((u - c) / sd, pm1, beta);
-                        acc += c - (xv - we) * sd;
+                        for (int i = 0; i < EB; ++i) {
+                            const double xv = h2f(xs[chunk_at<C::NS>(j, c0 + (i >> 3)) + (i & 7)]);
+                            const double u = fma(xv, sd, zd);
+                            const double c = fmin(fmax(rint(u), 0.0), qm);
+                            const double we = shrink((u - c) / sd, pm1, beta);
+                            acc += c - (xv - we) * sd;
+                        }
+                        acc = addd_k<KB>(acc);
+                        if (bleader) {
+                            st_z[j] = (float)(acc * (1.0 / G));
+                            st_beta[j] = st_beta[j] * a.kappa;
+                            st_t[j] = (uint8_t)(st_t[j] + 1);
+                            st_fl[j] = fl & kSbExact;
+                        }
+                        out = kNext;
                     }
-                    acc = addd_k<K>(acc);
-                    if (leader) {
-                        st_z[slot] = (float)(acc * (1.0 / G));
-                        st_beta[slot] = st_beta[slot] * a.kappa;
-                        st_t[slot] = (uint8_t)(st_t[slot] + 1);
-                        st_fl[slot] = fl & 1;
-                    }
-                    out = kActive;
                 }
+                push_batch(valid, out, j);
+                continue;
             }
-            push(valid, out, slot);
-            continue;
-        }
 
-        if (act_n > 0) {
-            // ================= PASS: evaluate up to GPI active groups =====================
-            const int n = act_n < GPI ? (int)act_n : GPI;
-            const bool valid = k < n;
-            uint8_t slot = 0;
-            if (valid) slot = ring_act[(act_h + k) & RM];
-            act_h = (act_h + n) & RM;
-            act_n -= n;
-            uint32_t xr[W];
-            float z = 0.f, s = 1.f, Sb = 0.f;
-            uint8_t fl = 0;
-            bool clampfree = true;
-            if (valid) {
-                z = st_z[slot];
-                s = st_s[slot];
-                Sb = (float)st_Sb[slot];
-                fl = st_fl[slot];
-                const uint32_t mm = st_mnmx[slot];
-                const uint4 *src = reinterpret_cast<const uint4 *>(xs + slot * G + sub * E);
-#pragma unroll
-                for (int i = 0; i < E / 8; ++i) {
-                    const uint4 v = src[i];
-                    xr[4 * i] = v.x;
-                    xr[4 * i + 1] = v.y;
-                    xr[4 * i + 2] = v.z;
-                    xr[4 * i + 3] = v.w;
-                }
-                const float ulo = fmaf(h2f(mm & 0xffffu), s, z);
-                const float uhi = fmaf(h2f(mm >> 16), s, z);
-                clampfree = ulo >= -0.5f && uhi < C::QMAX + 0.5f;
-            }
-            const bool any_clamp = __ballot(valid && !clampfree) != 0;
-            uint8_t out = kFinished;
-            if (valid) {
-                float S, Q, D;
-                if (any_clamp) eval_fast<NBITS, G, true>(xr, s, z, S, Q, D);
-                else eval_fast<NBITS, G, false>(xr, s, z, S, Q, D);
-                S = addf_k<K>(S);
-                Q = addf_k<K>(Q);
-                D = maxf_k<K>(D);
-                bool accept = false;
-                if (D >= C::kThr) {
-                    if (leader) st_fl[slot] = (uint8_t)((fl & 1) | (kDecide << 1));
-                    out = kExact;
-                } else if (!a.early_stop) {
-                    accept = true;
-                } else {
-                    // |S - S_exact| bounds (binary32 sums: G half-ulps of u plus the relative
-                    // summation error; clamped elements may sit above 2^NBITS where the ulp is
-                    // larger, so a clamped pass takes a wider bound). The margins are far above
-                    // the binary32 rounding of this comparison itself.
-                    const float em = any_clamp ? 4.0f * (float)C::kElemErr : (float)C::kElemErr;
-                    const float m = em + S * 0x1p-18f +
-                                    ((fl & 1) ? 0x1p-18f * Sb : 4.0f * (float)C::kElemErr + Sb * 0x1p-18f);
-                    if (S > Sb + m) out = kFinished;
-                    else if (S < Sb - m) accept = true;
-                    else {
-                        if (leader) st_fl[slot] = (uint8_t)((fl & 1) | (kDecide << 1));
-                        out = kExact;
+            if (can_init && (rdy_n < n_empty + n_hold || idle)) break;   // INIT, below
+
+            if (!idle) {
+                // ================= PASS: every lane with a group evaluates it ================
+                if (status == kActive) {
+                    // Codes stay in range when the group's extreme weights do: u of the min (max)
+                    // weight at least -1/2 (below 2^NBITS - 1/2). A binary32 bound that is off by
+                    // its rounding puts that weight next to a rounding boundary, where the D test
+                    // below hands the group to the exact path anyway. Groups that may clamp (about
+                    // one evaluation in 10^5) take the exact path.
+                    const float ulo = fmaf(h2f(g_mnmx & 0xffffu), g_s, g_z);
+                    const float uhi = fmaf(h2f(g_mnmx >> 16), g_s, g_z);
+                    if (!(ulo >= -0.5f && uhi < C::QMAX + 0.5f)) {
+                        g_fl = (g_fl & (kSbExact | kFirst)) | (kDecide << 1);
+                        status = kHoldExq;
                     }
                 }
-                if (accept) {
-                    if (leader) {
-                        st_zb[slot] = z;
-                        st_Sb[slot] = S;
-                        st_Qb[slot] = Q;
-                        st_Db[slot] = D;
-                        st_fl[slot] = 0;
+                if (status == kActive) {
+                    float S, T, D;
+                    eval_fast<NBITS, WP>(xr, g_s, g_z, S, T, D);
+                    if (KP == 2) {
+                        S = addf_k<2>(S);
+                        T = addf_k<2>(T);
+                        D = maxf_k<2>(D);
                     }
-                    out = advance(slot, s, z, Q, D, false);
+                    const float Q = (float)rint(fma((double)G, (double)g_z, g_X) - (double)T);
+                    const bool first = g_fl & kFirst;
+                    bool accept = false;
+                    uint32_t next = kActive;
+                    if (D >= C::kThr) {
+                        g_fl = (g_fl & (kSbExact | kFirst)) | (kDecide << 1);
+                        next = kHoldExq;
+                    } else if (first || !a.early_stop) {
+                        accept = true;
+                    } else {
+                        // |S - S_exact| bounds (binary32 sums: G half-ulps of u plus the relative
+                        // summation error). The margins are far above the binary32 rounding of this
+                        // comparison itself.
+                        const float Sb = (float)g_Sb;
+                        const float m = (float)C::kElemErr + S * 0x1p-18f +
+                                        ((g_fl & kSbExact) ? 0x1p-18f * Sb
+                                                           : 4.0f * (float)C::kElemErr + Sb * 0x1p-18f);
+                        if (S > Sb + m) next = kHoldFin;
+                        else if (S < Sb - m) accept = true;
+                        else {
+                            g_fl = (g_fl & kSbExact) | (kDecide << 1);
+                            next = kHoldExq;
+                        }
+                    }
+                    if (accept) {
+                        g_zb = g_z;
+                        g_Sb = S;
+                        g_Qb = Q;
+                        g_Db = D;
+                        g_fl = 0;
+                        const Advance ad = advance_core<NBITS, G>((int)g_t, a.iters, g_s, g_z, Q, D,
+                                                                  false, g_X, tau, tau_min);
+                        if (ad.out == kDone) {
+                            g_zb = ad.zn;
+                            next = kHoldFin;
+                        } else if (ad.out == kNeedShrink) {
+                            g_fl = kShrink << 1;
+                            next = kHoldExq;
+                        } else {
+                            g_z = ad.zn;
+                            g_beta = g_beta * a.kappa;
+                            g_t = g_t + 1;
+                        }
+                    }
+                    status = next;
                 }
+                continue;
             }
-            push(valid, out, slot);
-            continue;
+
+            done = true;                             // nothing left: every ring and lane is empty
+            break;
         }
-        break;
+        if (done) break;
+        // ================= INIT: a prefetched tile becomes ready groups ===============
+        budget += 8 * (int64_t)(a.iters + 4) * GB;
+        const int nv = pf_nv;
+        const bool valid = k < nv;
+        uint8_t j = 0;
+        if (valid) j = ring_free[(fre_h + k) & RM];
+        fre_h = (fre_h + nv) & RM;
+        fre_n -= nv;
+        if (valid) {
+            uint32_t xb[WB];
+#pragma unroll
+            for (int i = 0; i < EB / 8; ++i) {
+                const u32x4 v = pf[i];
+                *reinterpret_cast<u32x4 *>(xs + chunk_at<C::NS>(j, sub * (EB / 8) + i)) = v;
+                xb[4 * i] = v.x;
+                xb[4 * i + 1] = v.y;
+                xb[4 * i + 2] = v.z;
+                xb[4 * i + 3] = v.w;
+            }
+            // min / max on binary16 pairs, then across the group
+            h2v hmn = __builtin_bit_cast(h2v, xb[0]), hmx = hmn;
+#pragma unroll
+            for (int i = 1; i < WB; ++i) {
+                const h2v h = __builtin_bit_cast(h2v, xb[i]);
+                hmn = __builtin_elementwise_min(hmn, h);
+                hmx = __builtin_elementwise_max(hmx, h);
+            }
+            float mn = fminf((float)hmn.x, (float)hmn.y);
+            float mx = fmaxf((float)hmx.x, (float)hmx.y);
+            mn = minf_k<KB>(mn);
+            mx = maxf_k<KB>(mx);
+            const float rng = mx - mn;
+            const float s = rng > 0.0f ? C::QMAX / rng : 1.0f;
+            const float z0 = 0.0f - mn * s;      // +0 when min is a zero of either sign
+            const double sd = s;
+            double sxs = 0.0;
+#pragma unroll
+            for (int i = 0; i < EB; ++i)
+                sxs = fma((double)h2f(i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu), sd, sxs);
+            sxs = addd_k<KB>(sxs);
+            if (bleader) {
+                st_z[j] = z0;
+                st_zb[j] = z0;
+                st_s[j] = s;
+                float beta0 = a.beta0;
+                asm volatile("" : "+s"(beta0));     // kept in a scalar register until here
+                st_beta[j] = beta0;
+                st_Qb[j] = 0.f;
+                st_Db[j] = 0.f;
+                st_Sb[j] = 0.0;
+                st_X[j] = sxs;
+                st_mnmx[j] = (uint32_t)f2h(mn) | ((uint32_t)f2h(mx) << 16);
+                st_gidx[j] = (uint32_t)(pf_g0 + k);
+                st_job[j] = (uint16_t)pf_job;
+                st_t[j] = 1;
+                st_fl[j] = kFirst;
+            }
+        }
+        push_batch(valid, kNext, j);
+        prefetch();
     }
     flush_minmax();
 }
