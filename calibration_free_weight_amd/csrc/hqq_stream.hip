@@ -128,11 +128,15 @@ __device__ __forceinline__ uint32_t fkey(float f)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// pow for the rare paths (the shrink and its dead-zone threshold). Out of line: inlined, its
+// constants would be hoisted into registers for the whole solver loop.
+__device__ __attribute__((noinline)) double pow_ool(double a, double e) { return pow(a, e); }
+
 __device__ __forceinline__ double shrink(double r, double pm1, double beta)
 {
     if (r == 0.0) return 0.0;
     const double a = fabs(r);
-    const double m = fmax(a - pow(a, pm1) / beta, 0.0);
+    const double m = fmax(a - pow_ool(a, pm1) / beta, 0.0);
     return r > 0.0 ? m : -m;
 }
 
@@ -149,8 +153,18 @@ struct Cfg {
     static constexpr int GB = 64 / KB;              // groups per batch (one tile)
     static constexpr int WB = EB / 2;
     static constexpr int NC = G / 8;                // 16-byte chunks per group
-    static constexpr int NS = (G <= 32 ? 2 : 3) * GB;   // staging slots in LDS
-    static constexpr int RC = NS <= 64 ? 64 : (NS <= 128 ? 128 : 256);   // ring capacity
+    // Waves per SIMD the registers allow, and the staging slots that fit that many waves'
+    // LDS: 160 KB per compute unit, taken per wave in blocks of 1280 bytes (measured: 12,584
+    // bytes per wave let 12 waves share a compute unit, 13,032 only 11), holds each slot's
+    // weights and 52 bytes of state, the rings and the 3-bit code stage; at most three
+    // batches of slots.
+    static constexpr int WAVES = G <= 16 ? 4 : (G <= 128 ? 3 : 2);
+    static constexpr int RC = GB >= 32 ? 128 : 64;  // ring capacity
+    static constexpr int LDS_WAVE = 163840 / (4 * WAVES) / 1280 * 1280;
+    static constexpr int LDS_FREE = LDS_WAVE - 4 * RC - (NBITS == 3 ? 64 * EB : 0) - 128;
+    static constexpr int NS_FIT = LDS_FREE / (2 * G + 52);
+    static constexpr int NS = NS_FIT < 3 * GB ? NS_FIT : 3 * GB;   // staging slots
+    static_assert(NS >= GB + 4 && NS <= RC, "staging slots");
     static constexpr float QMAX = (float)((1 << NBITS) - 1);
     // A binary32 code can disagree with the exact one only if |u - rne(u)| >= kThr.
     static constexpr float kThr = 0.5f - (float)(1.0 / (1 << (24 - NBITS)));
@@ -231,8 +245,8 @@ struct Advance {
 };
 template <int NBITS, int G>
 __device__ __forceinline__ Advance advance_core(int t, int iters, float s, float zb, float Qb,
-                                                float Db, bool sbx, double X, const float *tau,
-                                                float tau_min)
+                                                float Db, bool sbx, double X, float beta,
+                                                float tau_min, double tau_exp)
 {
     using C = Cfg<NBITS, G>;
     if (t > iters) return Advance{kDone, zb};
@@ -242,14 +256,18 @@ __device__ __forceinline__ Advance advance_core(int t, int iters, float s, float
     // later iteration.
     const float dmax = sbx ? Db : Db + (0.5f - C::kThr);
     const bool dead_all = dmax <= tau_min * s;
-    if (!dead_all && !(dmax <= tau[t - 1] * (s * (1.0f - 4e-6f)))) return Advance{kNeedShrink, zb};
+    if (!dead_all) {
+        // this iteration's threshold, from the group's beta (beta0*kappa^(t-1))
+        const float tau_t = (float)pow_ool((double)beta, tau_exp);
+        if (!(dmax <= tau_t * (s * (1.0f - 4e-6f)))) return Advance{kNeedShrink, zb};
+    }
     const float zn = (float)(((double)Qb - X) * (1.0 / G));
     if (zn == zb && dead_all) return Advance{kDone, zn};   // exact fixed point
     return Advance{kNext, zn};
 }
 
 template <int NBITS, int G>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Cfg<NBITS, G>::WAVES)))
 stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 {
     using C = Cfg<NBITS, G>;
@@ -275,7 +293,6 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     __shared__ uint8_t rings[4 * C::RC];   // slot rings: ready, finished, exact-pending, free
     uint8_t *const ring_rdy = rings, *const ring_fin = rings + C::RC,
                    *const ring_exq = rings + 2 * C::RC, *const ring_free = rings + 3 * C::RC;
-    __shared__ float tau[kMaxIters];
     __shared__ __attribute__((aligned(4))) uint8_t stage[NBITS == 3 ? 64 * EB : 4];
 
     const int lane = threadIdx.x;
@@ -288,18 +305,17 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     const bool pleader = part == 0;
     const int pbase = lane - part;               // the group's first lane
 
-    // Dead-zone thresholds: the shrink of iteration t uses beta_{t-1} = beta0*kappa^(t-1)
-    // (binary32 products in order) and maps r to 0 iff |r| <= beta^(-1/(2-p)).
-    for (int t = lane; t < a.iters; t += 64) {
-        float b = a.beta0;
-        for (int i = 0; i < t; ++i) b = b * a.kappa;
-        tau[t] = (float)pow((double)b, -1.0 / (2.0 - (double)a.p));
-    }
+    // Dead zone of the shrink: iteration t uses beta_{t-1} = beta0*kappa^(t-1) (binary32
+    // products in order) and maps r to 0 iff |r| <= beta^(-1/(2-p)). The smallest threshold
+    // (the last iteration's) settles most groups for every iteration at once.
+    const double tau_exp = -1.0 / (2.0 - (double)a.p);
+    float beta_last = a.beta0;
+    for (int i = 1; i < a.iters; ++i) beta_last = beta_last * a.kappa;
+    const float tau_min = __builtin_bit_cast(
+        float, uniform(__float_as_uint(
+                   a.iters > 0 ? (float)pow_ool((double)beta_last, tau_exp) * (1.0f - 4e-6f) : 0.0f)));
     for (int i = lane; i < NS; i += 64) ring_free[i] = (uint8_t)i;
     __syncthreads();
-    // wave-uniform: kept in a scalar register
-    const float tau_min = __builtin_bit_cast(
-        float, uniform(__float_as_uint(a.iters > 0 ? tau[a.iters - 1] * (1.0f - 4e-6f) : 0.0f)));
     const double pm1 = (double)a.p - 1.0;
 
     uint32_t rdy_h = 0, rdy_n = 0, fin_h = 0, fin_n = 0, exq_h = 0, exq_n = 0, fre_h = 0, fre_n = NS;
@@ -386,8 +402,8 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     // Batch version of the advance step, on slot j (fields written by the group's leader).
     auto advance_slot = [&](uint8_t j, float s, float zb, float Qb, float Db, bool sbx) -> uint8_t {
         const int t = st_t[j];
-        const Advance ad = advance_core<NBITS, G>(t, a.iters, s, zb, Qb, Db, sbx, st_X[j], tau,
-                                                  tau_min);
+        const Advance ad = advance_core<NBITS, G>(t, a.iters, s, zb, Qb, Db, sbx, st_X[j],
+                                                  st_beta[j], tau_min, tau_exp);
         if (bleader) {
             if (ad.out == kDone) st_zb[j] = ad.zn;
             else if (ad.out == kNeedShrink) st_fl[j] = (uint8_t)((sbx ? kSbExact : 0) | (kShrink << 1));
@@ -847,7 +863,8 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                         g_Db = D;
                         g_fl = 0;
                         const Advance ad = advance_core<NBITS, G>((int)g_t, a.iters, g_s, g_z, Q, D,
-                                                                  false, g_X, tau, tau_min);
+                                                                  false, g_X, g_beta, tau_min,
+                                                                  tau_exp);
                         if (ad.out == kDone) {
                             g_zb = ad.zn;
                             next = kHoldFin;
