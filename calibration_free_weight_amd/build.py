@@ -8,6 +8,9 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libhqq.so")
+# The same library with a minimal staging pool (one batch plus four slots): the tests run it
+# so that the solver's rare pool-full paths (a lane exchanging its group in place) execute.
+STRESS_LIB = os.path.join(PKG, "libhqq_stress.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -22,15 +25,21 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
+def _compile(out: str, extra, verbose: bool) -> None:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(PKG, "csrc"), "-o", tmp, *sources()]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, stress: bool = True) -> str:
+    _compile(LIB, [], verbose)
+    if stress:
+        _compile(STRESS_LIB, ["-DHQQ_STRESS_SLOTS=4"], verbose)
     return LIB
 
 

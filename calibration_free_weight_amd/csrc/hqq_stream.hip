@@ -162,8 +162,15 @@ struct Cfg {
     static constexpr int RC = GB >= 32 ? 128 : 64;  // ring capacity
     static constexpr int LDS_WAVE = 163840 / (4 * WAVES) / 1280 * 1280;
     static constexpr int LDS_FREE = LDS_WAVE - 4 * RC - (NBITS == 3 ? 64 * EB : 0) - 128;
-    static constexpr int NS_FIT = LDS_FREE / (2 * G + 52);
+    static constexpr int NS_FIT = (LDS_FREE - 16 * NC) / (2 * G + 52);   // one spare column
+#ifdef HQQ_STRESS_SLOTS
+    // stress build for the tests: a pool of one batch plus a few slots, so that lanes must
+    // often exchange their group with a ready one
+    static constexpr int NS = GB + HQQ_STRESS_SLOTS;
+#else
     static constexpr int NS = NS_FIT < 3 * GB ? NS_FIT : 3 * GB;   // staging slots
+#endif
+    static constexpr int CS = NS | 1;               // chunk stride (odd)
     static_assert(NS >= GB + 4 && NS <= RC, "staging slots");
     static constexpr float QMAX = (float)((1 << NBITS) - 1);
     // A binary32 code can disagree with the exact one only if |u - rne(u)| >= kThr.
@@ -203,13 +210,14 @@ __device__ __forceinline__ void eval_fast(const uint32_t (&xr)[N], float s, floa
     asm volatile("" : "+v"(S), "+v"(T), "+v"(D));
 }
 
-// LDS position (in binary16 elements) of 16-byte chunk c of staging slot j among NS slots:
-// chunk-major, so a lane walks its slot at a constant stride (immediate offsets) and lanes
-// reading the same chunk of different slots touch neighbouring 16-byte words.
-template <int NS>
+// LDS position (in binary16 elements) of 16-byte chunk c of staging slot j, chunk-major with
+// a stride of CS chunks: a lane walks its slot at a constant stride (immediate offsets),
+// lanes reading the same chunk of different slots touch neighbouring 16-byte words, and with
+// CS odd the lanes that read consecutive quarters of one group land in different banks.
+template <int CS>
 __device__ __forceinline__ int chunk_at(int j, int c)
 {
-    return (c * NS + j) << 3;
+    return (c * CS + j) << 3;
 }
 
 struct Exact {
@@ -226,7 +234,7 @@ __device__ __forceinline__ Exact eval_exact(const uint16_t *xs, int j, int c0, f
     double s_ = 0.0, q_ = 0.0, d_ = 0.0;
 #pragma unroll 1
     for (int i = 0; i < C::EB; ++i) {
-        const double u = fma((double)h2f(xs[chunk_at<C::NS>(j, c0 + (i >> 3)) + (i & 7)]), sd, zd);
+        const double u = fma((double)h2f(xs[chunk_at<C::CS>(j, c0 + (i >> 3)) + (i & 7)]), sd, zd);
         const double c = fmin(fmax(rint(u), 0.0), qm);
         const double e = fabs(u - c);
         s_ += e;
@@ -276,7 +284,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     static_assert(NS <= 255, "slot indices are bytes");
 
     // Staging slots: weights and per-group state (one array per field).
-    __shared__ __attribute__((aligned(16))) uint16_t xs[NS * G];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[C::CS * G];
     __shared__ float st_z[NS];         // candidate zero (next evaluation)
     __shared__ float st_zb[NS];        // accepted zero
     __shared__ float st_s[NS];         // quantizer multiplier
@@ -560,7 +568,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 float u[EB];
 #pragma unroll
                 for (int c = 0; c < EB / 8; ++c) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::NS>(j, sub * (EB / 8) + c));
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(j, sub * (EB / 8) + c));
                     const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
@@ -574,7 +582,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 #pragma unroll 1
                 for (int i = 0; i < EB; ++i) {
                     const int c = sub * (EB / 8) + (i >> 3);
-                    const double u = fma((double)h2f(xs[chunk_at<C::NS>(j, c) + (i & 7)]), (double)s, (double)zb);
+                    const double u = fma((double)h2f(xs[chunk_at<C::CS>(j, c) + (i & 7)]), (double)s, (double)zb);
                     const float cf = (float)fmin(fmax(rint(u), 0.0), (double)C::QMAX);
 #pragma unroll
                     for (int m = 0; m < EB; ++m)
@@ -682,7 +690,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 if (n_x > 0 && exch_l) {
 #pragma unroll
                     for (int c = 0; c < WP / 4; ++c) {
-                        u32x4 *q = reinterpret_cast<u32x4 *>(xs + chunk_at<C::NS>(jo, part * (WP / 4) + c));
+                        u32x4 *q = reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(jo, part * (WP / 4) + c));
                         const u32x4 v = *q;
                         *q = u32x4{xr[4 * c], xr[4 * c + 1], xr[4 * c + 2], xr[4 * c + 3]};
                         xr[4 * c] = v.x;
@@ -697,14 +705,14 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 if (out_l) {
 #pragma unroll
                     for (int c = 0; c < WP / 4; ++c)
-                        *reinterpret_cast<u32x4 *>(xs + chunk_at<C::NS>(jo, part * (WP / 4) + c)) =
+                        *reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(jo, part * (WP / 4) + c)) =
                             u32x4{xr[4 * c], xr[4 * c + 1], xr[4 * c + 2], xr[4 * c + 3]};
                     if (lead) save_state(jo);
                 }
                 if (in_l) {
 #pragma unroll
                     for (int c = 0; c < WP / 4; ++c) {
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::NS>(ji, part * (WP / 4) + c));
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(ji, part * (WP / 4) + c));
                         xr[4 * c] = v.x;
                         xr[4 * c + 1] = v.y;
                         xr[4 * c + 2] = v.z;
@@ -787,7 +795,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                         double acc = 0.0;
 #pragma unroll 1
                         for (int i = 0; i < EB; ++i) {
-                            const double xv = h2f(xs[chunk_at<C::NS>(j, c0 + (i >> 3)) + (i & 7)]);
+                            const double xv = h2f(xs[chunk_at<C::CS>(j, c0 + (i >> 3)) + (i & 7)]);
                             const double u = fma(xv, sd, zd);
                             const double c = fmin(fmax(rint(u), 0.0), qm);
                             const double we = shrink((u - c) / sd, pm1, beta);
@@ -899,7 +907,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 #pragma unroll
             for (int i = 0; i < EB / 8; ++i) {
                 const u32x4 v = pf[i];
-                *reinterpret_cast<u32x4 *>(xs + chunk_at<C::NS>(j, sub * (EB / 8) + i)) = v;
+                *reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(j, sub * (EB / 8) + i)) = v;
                 xb[4 * i] = v.x;
                 xb[4 * i + 1] = v.y;
                 xb[4 * i + 2] = v.z;

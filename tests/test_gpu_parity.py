@@ -4,6 +4,7 @@ import pytest
 import torch
 
 from tests.conftest import has_gpu
+import synth
 from tests.gpu_util import compare, u16, u8, weights
 
 pytestmark = pytest.mark.gpu
@@ -91,6 +92,61 @@ def test_edge_inputs(O, dev):
             g = 16
             out = run(W, nbits, g)
             compare(O, W, out, nbits, g, 16, label=name)
+
+
+def half_grid_groups(rows, cols, g, nbits, seed, frac=1.0):
+    """Groups whose first evaluation lands exactly on rounding boundaries: each group holds
+    its min 0, its max qmax/16 and otherwise values (k + 1/2)/16, so s = 16, z0 = 0 and
+    u = k + 1/2 (ties to even). A fraction `frac` of the groups is built this way, the rest
+    are ordinary weights. Every such group needs the exact path at its first evaluation."""
+    qmax = (1 << nbits) - 1
+    gen = torch.Generator().manual_seed(seed)
+    ng = rows * cols // g
+    W = synth.student_t_weights(rows, cols, seed).reshape(ng, g).clone()
+    k = torch.randint(0, qmax, (ng, g), generator=gen).float()
+    grid = ((k + 0.5) / 16.0).half()
+    grid[:, 0] = 0.0
+    grid[:, 1] = qmax / 16.0
+    perm = torch.argsort(torch.rand(ng, g, generator=gen), dim=1)
+    grid = torch.gather(grid, 1, perm)
+    pick = torch.rand(ng, generator=gen) < frac
+    W[pick] = grid[pick]
+    return W.reshape(rows, cols)
+
+
+@pytest.mark.parametrize("frac", [1.0, 0.5])
+@pytest.mark.parametrize("nbits,g", [(4, 128), (4, 64), (2, 16), (3, 64), (8, 256)])
+def test_boundary_groups_take_exact_path(O, dev, nbits, g, frac):
+    """Every first evaluation of these groups is a tie of codes: the batch of exact-path
+    groups fills the staging slots, so groups are exchanged between lanes and slots."""
+    rows, cols = 48, g * 32
+    print(f"boundary groups nbits={nbits} g={g} frac={frac}", flush=True)
+    W = half_grid_groups(rows, cols, g, nbits, 11 + nbits + g, frac).to(dev)
+    for zero_bits in (16, 8):
+        out = run(W, nbits, g, zero_bits)
+        compare(O, W, out, nbits, g, zero_bits, label=f"grid b{nbits} g{g} z{zero_bits}")
+
+
+def test_minimal_staging_pool(O, dev):
+    """The stress build of the library (a pool of one batch plus four slots) must give the
+    same results: lanes then exchange groups with ready ones in place, a path the normal
+    pool size rarely needs."""
+    import os
+    from calibration_free_weight_amd import build as hbuild
+    assert os.path.exists(hbuild.STRESS_LIB), "build the library (stress build included) first"
+    saved = hqq.LIB_PATH, hqq._L
+    hqq.LIB_PATH, hqq._L = hbuild.STRESS_LIB, None
+    try:
+        cases = [(4, 128, 1.0), (4, 128, 0.5), (2, 16, 1.0), (4, 64, 0.0), (3, 64, 0.3),
+                 (8, 256, 0.0)]
+        for nbits, g, frac in cases:
+            print(f"stress pool nbits={nbits} g={g} frac={frac}", flush=True)
+            W = half_grid_groups(48, g * 32, g, nbits, 5 + nbits + g, frac).to(dev)
+            for zero_bits in (16, 8):
+                out = run(W, nbits, g, zero_bits)
+                compare(O, W, out, nbits, g, zero_bits, label=f"stress b{nbits} g{g}")
+    finally:
+        hqq.LIB_PATH, hqq._L = saved
 
 
 def test_empty_tensor(dev):
