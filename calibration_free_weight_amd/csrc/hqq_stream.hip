@@ -162,7 +162,8 @@ struct Cfg {
     static constexpr int RC = GB >= 32 ? 128 : 64;  // ring capacity
     static constexpr int LDS_WAVE = 163840 / (4 * WAVES) / 1280 * 1280;
     static constexpr int LDS_FREE = LDS_WAVE - 4 * RC - (NBITS == 3 ? 64 * EB : 0) - 128;
-    static constexpr int NS_FIT = (LDS_FREE - 16 * NC) / (2 * G + 52);   // one spare column
+    // the spare slot and one more column (for an odd stride) come out of the budget first
+    static constexpr int NS_FIT = (LDS_FREE - 2 * (2 * G + 52)) / (2 * G + 52);
 #ifdef HQQ_STRESS_SLOTS
     // stress build for the tests: a pool of one batch plus a few slots, so that lanes must
     // often exchange their group with a ready one
@@ -170,7 +171,7 @@ struct Cfg {
 #else
     static constexpr int NS = NS_FIT < 3 * GB ? NS_FIT : 3 * GB;   // staging slots
 #endif
-    static constexpr int CS = NS | 1;               // chunk stride (odd)
+    static constexpr int CS = (NS + 1) | 1;         // chunk stride: slots and spare, odd
     static_assert(NS >= GB + 4 && NS <= RC, "staging slots");
     static constexpr float QMAX = (float)((1 << NBITS) - 1);
     // A binary32 code can disagree with the exact one only if |u - rne(u)| >= kThr.
@@ -281,23 +282,24 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     using C = Cfg<NBITS, G>;
     constexpr int KP = C::KP, WP = C::WP, EB = C::EB, KB = C::KB, GB = C::GB, WB = C::WB;
     constexpr int NS = C::NS, RM = C::RC - 1;
+    constexpr int kSpare = NS;                   // the spare slot (in no ring)
     static_assert(NS <= 255, "slot indices are bytes");
 
-    // Staging slots: weights and per-group state (one array per field).
+    // Staging slots and the spare: weights and per-group state (one array per field).
     __shared__ __attribute__((aligned(16))) uint16_t xs[C::CS * G];
-    __shared__ float st_z[NS];         // candidate zero (next evaluation)
-    __shared__ float st_zb[NS];        // accepted zero
-    __shared__ float st_s[NS];         // quantizer multiplier
-    __shared__ float st_beta[NS];      // beta of the next shrink
-    __shared__ float st_Qb[NS];        // accepted sum of codes
-    __shared__ float st_Db[NS];        // accepted max |u - q|
-    __shared__ double st_Sb[NS];       // accepted sum |u - q|
-    __shared__ double st_X[NS];        // exact sum x*s
-    __shared__ uint32_t st_mnmx[NS];   // binary16 min (low half) and max (high half)
-    __shared__ uint32_t st_gidx[NS];   // group index within its tensor
-    __shared__ uint16_t st_job[NS];    // job index within the launch class
-    __shared__ uint8_t st_t[NS];       // index of the next zero update (1-based)
-    __shared__ uint8_t st_fl[NS];      // flags (kSbExact | work << 1 | kFirst)
+    __shared__ float st_z[NS + 1];         // candidate zero (next evaluation)
+    __shared__ float st_zb[NS + 1];        // accepted zero
+    __shared__ float st_s[NS + 1];         // quantizer multiplier
+    __shared__ float st_beta[NS + 1];      // beta of the next shrink
+    __shared__ float st_Qb[NS + 1];        // accepted sum of codes
+    __shared__ float st_Db[NS + 1];        // accepted max |u - q|
+    __shared__ double st_Sb[NS + 1];       // accepted sum |u - q|
+    __shared__ double st_X[NS + 1];        // exact sum x*s
+    __shared__ uint32_t st_mnmx[NS + 1];   // binary16 min (low half) and max (high half)
+    __shared__ uint32_t st_gidx[NS + 1];   // group index within its tensor
+    __shared__ uint16_t st_job[NS + 1];    // job index within the launch class
+    __shared__ uint8_t st_t[NS + 1];       // index of the next zero update (1-based)
+    __shared__ uint8_t st_fl[NS + 1];      // flags (kSbExact | work << 1 | kFirst)
     __shared__ uint8_t rings[4 * C::RC];   // slot rings: ready, finished, exact-pending, free
     uint8_t *const ring_rdy = rings, *const ring_fin = rings + C::RC,
                    *const ring_exq = rings + 2 * C::RC, *const ring_free = rings + 3 * C::RC;
@@ -435,20 +437,24 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
         return GroupState{st_s[j], st_z[j], st_zb[j], st_Qb[j], st_Db[j], st_beta[j], st_Sb[j],
                           st_X[j], st_mnmx[j], st_gidx[j], st_job[j], st_t[j], st_fl[j]};
     };
-    auto save_state = [&](int j) {
-        st_s[j] = g_s;
-        st_z[j] = g_z;
-        st_zb[j] = g_zb;
-        st_Qb[j] = g_Qb;
-        st_Db[j] = g_Db;
-        st_beta[j] = g_beta;
-        st_Sb[j] = g_Sb;
-        st_X[j] = g_X;
-        st_mnmx[j] = g_mnmx;
-        st_gidx[j] = g_gidx;
-        st_job[j] = (uint16_t)g_job;
-        st_t[j] = (uint8_t)g_t;
-        st_fl[j] = (uint8_t)g_fl;
+    auto put_state = [&](int j, const GroupState &n) {
+        st_s[j] = n.s;
+        st_z[j] = n.z;
+        st_zb[j] = n.zb;
+        st_Qb[j] = n.Qb;
+        st_Db[j] = n.Db;
+        st_beta[j] = n.beta;
+        st_Sb[j] = n.Sb;
+        st_X[j] = n.X;
+        st_mnmx[j] = n.mnmx;
+        st_gidx[j] = n.gidx;
+        st_job[j] = (uint16_t)n.job;
+        st_t[j] = (uint8_t)n.t;
+        st_fl[j] = (uint8_t)n.fl;
+    };
+    auto cur_state = [&]() -> GroupState {
+        return GroupState{g_s, g_z, g_zb, g_Qb, g_Db, g_beta, g_Sb, g_X, g_mnmx, g_gidx, g_job,
+                          g_t, g_fl};
     };
     auto set_state = [&](const GroupState &n) {
         g_s = n.s;
@@ -510,35 +516,43 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             const float s = st_s[j];
             gidx = st_gidx[j];
             const int64_t e0 = (int64_t)gidx * G + sub * EB;   // first weight of this lane
-            // Packs this lane's EB codes and stores them. v[i] is either the exact code
-            // or a u whose code is rne(u) in [0, 2^NBITS - 1]: v_cvt_pk_u8_f32 rounds
-            // half to even and saturates to [0, 255], so either way it yields the code.
-            auto emit = [&](const float (&v)[EB]) {
-                // bytes of codes, then NBITS-bit fields: byte b of plane m holds code
-                // PL*b + m, so plane m shifts by NBITS*m (3-bit codes: one per byte)
+            // Packs this lane's EB codes and stores them, a 16-byte chunk of weights at a
+            // time. val(h) maps a weight's binary16 bits to either its exact code or a u whose
+            // code is rne(u) in [0, 2^NBITS - 1]: v_cvt_pk_u8_f32 rounds half to even and
+            // saturates to [0, 255], so either way it yields the code. Byte b of plane m of
+            // word q holds code PER*q + PL*b + m, so plane m shifts by NBITS*m (3-bit codes:
+            // one per byte, joined into words below).
+            auto emit = [&](auto val) {
                 constexpr int PL = NBITS == 3 ? 1 : 8 / NBITS;   // planes
                 constexpr int BY = EB / PL < 4 ? EB / PL : 4;    // bytes per word
                 constexpr int PER = BY * PL;           // codes per word
                 constexpr int NW = EB / PER;
+                uint32_t pl[NW][PL];
+#pragma unroll
+                for (int q = 0; q < NW; ++q)
+#pragma unroll
+                    for (int m = 0; m < PL; ++m) pl[q][m] = 0u;
+#pragma unroll
+                for (int c = 0; c < EB / 8; ++c) {
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(j, sub * (EB / 8) + c));
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int i = 8 * c + e;
+                        const uint32_t h = e & 1 ? w4[e >> 1] >> 16 : w4[e >> 1] & 0xffffu;
+                        const int q = i / PER, m = i % PL, b = (i % PER) / PL;
+                        pl[q][m] = __builtin_amdgcn_cvt_pk_u8_f32(val(h), b, pl[q][m]);
+                    }
+                }
                 uint32_t w[NW];
 #pragma unroll
                 for (int q = 0; q < NW; ++q) {
-                    uint32_t pl[PL];
+                    uint32_t word = pl[q][0];
 #pragma unroll
-                    for (int m = 0; m < PL; ++m) {
-                        uint32_t acc = 0;
-#pragma unroll
-                        for (int b = 0; b < BY; ++b)
-                            acc = __builtin_amdgcn_cvt_pk_u8_f32(v[PER * q + PL * b + m], b, acc);
-                        pl[m] = acc;
-                    }
-                    uint32_t word = pl[0];
-#pragma unroll
-                    for (int m = 1; m < PL; ++m) word |= pl[m] << (NBITS * m);
+                    for (int m = 1; m < PL; ++m) word |= pl[q][m] << (NBITS * m);
                     w[q] = word;
                 }
                 if constexpr (NBITS == 3) {
-                    // one code per byte into the stage; words are formed below
 #pragma unroll
                     for (int q = 0; q < NW; ++q)
                         *reinterpret_cast<uint32_t *>(stage + lane * EB + 4 * q) = w[q];
@@ -562,33 +576,14 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             };
             // The accepted evaluation ran in binary32 with the same operations (so its D
             // bounds these codes: none is next to a rounding boundary and none clamps)
-            // or in binary64; exact codes only if D was near 1/2. Each branch packs its
-            // own values, so they cross no join.
+            // or in binary64; exact codes only if D was near 1/2.
             if (st_Db[j] < C::kThr - (float)(1.0 / (1 << (24 - NBITS)))) {
-                float u[EB];
-#pragma unroll
-                for (int c = 0; c < EB / 8; ++c) {
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(j, sub * (EB / 8) + c));
-                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const uint32_t h = i & 1 ? w4[i >> 1] >> 16 : w4[i >> 1] & 0xffffu;
-                        u[8 * c + i] = fmaf(h2f(h), s, zb);
-                    }
-                }
-                emit(u);
+                emit([&](uint32_t h) { return fmaf(h2f(h), s, zb); });
             } else {
-                float code[EB];
-#pragma unroll 1
-                for (int i = 0; i < EB; ++i) {
-                    const int c = sub * (EB / 8) + (i >> 3);
-                    const double u = fma((double)h2f(xs[chunk_at<C::CS>(j, c) + (i & 7)]), (double)s, (double)zb);
-                    const float cf = (float)fmin(fmax(rint(u), 0.0), (double)C::QMAX);
-#pragma unroll
-                    for (int m = 0; m < EB; ++m)
-                        if (m == i) code[m] = cf;
-                }
-                emit(code);
+                emit([&](uint32_t h) {
+                    const double u = fma((double)h2f(h), (double)s, (double)zb);
+                    return (float)fmin(fmax(rint(u), 0.0), (double)C::QMAX);
+                });
             }
             if (bleader) {
                 gbl(J.scale)[gidx] = f2h(1.0f / s);
@@ -670,46 +665,45 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             if ((n_hold > 0 && (rdy_n > 0 || fre_n > 0)) || (n_empty > 0 && rdy_n > 0)) {
                 // ================= SWAP: groups leave lanes for slots and enter from slots ====
                 // Holders store their group in a free slot; lanes left without a group load a
-                // ready one. Only when no slot is free does a holder exchange its group with a
-                // ready one in place (chunk by chunk, read before write).
+                // ready one. When no slot is free, one holder exchanges its group with a ready
+                // one through the spare slot: the ready group is copied there, the holder's
+                // group takes its slot, and the holder loads from the spare like any other
+                // lane (so the weight registers have a single load site).
                 const uint32_t n_out = n_hold < fre_n ? n_hold : fre_n;
-                const uint32_t n_x = n_out < n_hold ? (n_hold - n_out < rdy_n ? n_hold - n_out : rdy_n) : 0;
+                const uint32_t n_x = (n_out < n_hold && fre_n == 0 && rdy_n > 0) ? 1u : 0u;
                 const uint32_t rk_h = group_rank(m_hold, pbase);
                 const bool out_l = holder && rk_h < n_out;
-                const bool exch_l = holder && rk_h >= n_out && rk_h - n_out < n_x;
+                const bool exch_l = n_x > 0 && holder && rk_h == n_out;
                 const bool no_group = status == kEmpty || out_l;
                 const uint64_t m_ng = __ballot(no_group && lead);
                 const uint32_t n_ng = (uint32_t)__builtin_popcountll(m_ng);
                 const uint32_t n_in = n_ng < rdy_n - n_x ? n_ng : rdy_n - n_x;
                 const uint32_t rk_n = group_rank(m_ng, pbase);
                 const bool in_l = no_group && rk_n < n_in;
-                int jo = -1, ji = -1;
+                const bool st = out_l || exch_l, ld = in_l || exch_l;
+                int jo = 0, ji = 0;
                 if (out_l) jo = ring_free[(fre_h + rk_h) & RM];
-                if (exch_l) jo = ring_rdy[(rdy_h + rk_h - n_out) & RM];
+                if (exch_l) jo = ring_rdy[rdy_h & RM];
                 if (in_l) ji = ring_rdy[(rdy_h + n_x + rk_n) & RM];
-                if (n_x > 0 && exch_l) {
+                if (exch_l) ji = kSpare;
+                if (n_x > 0 && exch_l) {             // the ready group moves to the spare slot
 #pragma unroll
                     for (int c = 0; c < WP / 4; ++c) {
-                        u32x4 *q = reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(jo, part * (WP / 4) + c));
-                        const u32x4 v = *q;
-                        *q = u32x4{xr[4 * c], xr[4 * c + 1], xr[4 * c + 2], xr[4 * c + 3]};
-                        xr[4 * c] = v.x;
-                        xr[4 * c + 1] = v.y;
-                        xr[4 * c + 2] = v.z;
-                        xr[4 * c + 3] = v.w;
+                        const int off = part * (WP / 4) + c;
+                        const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(jo, off));
+                        *reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(kSpare, off)) = v;
                     }
                     const GroupState ns = load_state(jo);
-                    if (lead) save_state(jo);
-                    set_state(ns);
+                    if (lead) put_state(kSpare, ns);
                 }
-                if (out_l) {
+                if (st) {
 #pragma unroll
                     for (int c = 0; c < WP / 4; ++c)
                         *reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(jo, part * (WP / 4) + c)) =
                             u32x4{xr[4 * c], xr[4 * c + 1], xr[4 * c + 2], xr[4 * c + 3]};
-                    if (lead) save_state(jo);
+                    if (lead) put_state(jo, cur_state());
                 }
-                if (in_l) {
+                if (ld) {
 #pragma unroll
                     for (int c = 0; c < WP / 4; ++c) {
                         const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(ji, part * (WP / 4) + c));
@@ -722,7 +716,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 }
                 // rings: stored groups go to finished / exact-pending; the slots of loaded
                 // groups become free
-                const bool stored = out_l || exch_l;
+                const bool stored = st;
                 const bool to_fin = stored && status == kHoldFin;
                 const uint64_t m_f = __ballot(to_fin && lead);
                 const uint64_t m_x = __ballot(stored && !to_fin && lead);
@@ -739,7 +733,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 fre_n += (uint32_t)__builtin_popcountll(m_fr);
                 fin_n += (uint32_t)__builtin_popcountll(m_f);
                 exq_n += (uint32_t)__builtin_popcountll(m_x);
-                if (in_l || exch_l) status = kActive;
+                if (ld) status = kActive;
                 else if (out_l) status = kEmpty;
                 continue;
             }
