@@ -193,18 +193,21 @@ def main():
     t1 = time.perf_counter()
     log("bench: timed steps done")
 
-    # Mean evaluations per group, from the solver's own per-group counts (untimed run).
-    n_pass, n_groups = 0, 0
+    # Mean evaluations per group, from the solver's own per-group counts: one more (untimed)
+    # solve of the whole batch with the count outputs set.
+    counts = []
     for s, j in zip(specs, job_sets[0]):
-        ng = s.numel // s.group_size
-        pb = torch.empty(ng, dtype=torch.uint8, device=dev)
+        pb = torch.empty(s.numel // s.group_size, dtype=torch.uint8, device=dev)
         j.passes = pb.data_ptr()
-        hqq.hqq_quantize_batch([j], ws, stream.cuda_stream)
-        n_pass += int(pb.sum(dtype=torch.int64).item())
-        n_groups += ng
-        j.passes = None
-        del pb
+        counts.append(pb)
+    hqq.hqq_solve_batch(job_sets[0], ws, stream.cuda_stream)
+    torch.cuda.synchronize()
+    n_pass = sum(int(pb.sum(dtype=torch.int64).item()) for pb in counts)
+    n_groups = sum(pb.numel() for pb in counts)
     mean_passes = n_pass / n_groups
+    for j in job_sets[0]:
+        j.passes = None
+    del counts
 
     sec_per_step = (t1 - t0) / args.steps
     value = 2.0 * n_weights / sec_per_step / 1e9
