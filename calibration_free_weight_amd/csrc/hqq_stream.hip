@@ -141,6 +141,27 @@ __device__ __forceinline__ double shrink(double r, double pm1, double beta)
 }
 
 
+// Solver state of a group in a staging slot, as three 16-byte records (one LDS array each, so a
+// group moves with three 128-bit accesses). meta packs the flags (bits 0-7), the index of the
+// next zero update (8-15) and the tensor (16-31).
+struct alignas(16) SlotA {
+    float s, z, zb, Db;      // quantizer multiplier, candidate zero, accepted zero, its max|u-q|
+};
+struct alignas(16) SlotB {
+    float beta;              // beta of the next shrink
+    uint32_t mnmx;           // binary16 min (low half) and max (high half)
+    uint32_t gidx;           // group index within its tensor
+    uint32_t meta;
+};
+struct alignas(16) SlotC {
+    double Sb;               // accepted sum |u - q|
+    double X;                // exact sum x*s
+};
+__device__ __forceinline__ uint32_t meta_fl(uint32_t m) { return m & 0xffu; }
+__device__ __forceinline__ uint32_t meta_t(uint32_t m) { return (m >> 8) & 0xffu; }
+__device__ __forceinline__ uint32_t meta_job(uint32_t m) { return m >> 16; }
+__device__ __forceinline__ uint32_t with_fl(uint32_t m, uint32_t fl) { return (m & ~0xffu) | fl; }
+
 template <int NBITS, int G>
 struct Cfg {
     // Pass layout: a lane owns a group (a lane pair when G = 256), EP weights per lane.
@@ -156,14 +177,14 @@ struct Cfg {
     // Waves per SIMD the registers allow, and the staging slots that fit that many waves'
     // LDS: 160 KB per compute unit, taken per wave in blocks of 1280 bytes (measured: 12,584
     // bytes per wave let 12 waves share a compute unit, 13,032 only 11), holds each slot's
-    // weights and 52 bytes of state, the rings and the 3-bit code stage; at most three
+    // weights and 48 bytes of state, the rings and the 3-bit code stage; at most three
     // batches of slots.
     static constexpr int WAVES = G <= 16 ? 4 : (G <= 128 ? 3 : 2);
     static constexpr int RC = GB >= 32 ? 128 : 64;  // ring capacity
     static constexpr int LDS_WAVE = 163840 / (4 * WAVES) / 1280 * 1280;
     static constexpr int LDS_FREE = LDS_WAVE - 4 * RC - (NBITS == 3 ? 64 * EB : 0) - 128;
     // the spare slot and one more column (for an odd stride) come out of the budget first
-    static constexpr int NS_FIT = (LDS_FREE - 2 * (2 * G + 52)) / (2 * G + 52);
+    static constexpr int NS_FIT = (LDS_FREE - 2 * (2 * G + 48)) / (2 * G + 48);
 #ifdef HQQ_STRESS_SLOTS
     // stress build for the tests: a pool of one batch plus a few slots, so that lanes must
     // often exchange their group with a ready one
@@ -287,19 +308,9 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 
     // Staging slots and the spare: weights and per-group state (one array per field).
     __shared__ __attribute__((aligned(16))) uint16_t xs[C::CS * G];
-    __shared__ float st_z[NS + 1];         // candidate zero (next evaluation)
-    __shared__ float st_zb[NS + 1];        // accepted zero
-    __shared__ float st_s[NS + 1];         // quantizer multiplier
-    __shared__ float st_beta[NS + 1];      // beta of the next shrink
-    __shared__ float st_Qb[NS + 1];        // accepted sum of codes
-    __shared__ float st_Db[NS + 1];        // accepted max |u - q|
-    __shared__ double st_Sb[NS + 1];       // accepted sum |u - q|
-    __shared__ double st_X[NS + 1];        // exact sum x*s
-    __shared__ uint32_t st_mnmx[NS + 1];   // binary16 min (low half) and max (high half)
-    __shared__ uint32_t st_gidx[NS + 1];   // group index within its tensor
-    __shared__ uint16_t st_job[NS + 1];    // job index within the launch class
-    __shared__ uint8_t st_t[NS + 1];       // index of the next zero update (1-based)
-    __shared__ uint8_t st_fl[NS + 1];      // flags (kSbExact | work << 1 | kFirst)
+    __shared__ SlotA st_a[NS + 1];
+    __shared__ SlotB st_b[NS + 1];
+    __shared__ SlotC st_c[NS + 1];
     __shared__ uint8_t rings[4 * C::RC];   // slot rings: ready, finished, exact-pending, free
     uint8_t *const ring_rdy = rings, *const ring_fin = rings + C::RC,
                    *const ring_exq = rings + 2 * C::RC, *const ring_free = rings + 3 * C::RC;
@@ -334,9 +345,9 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     uint32_t xr[WP];
 #pragma unroll
     for (int i = 0; i < WP; ++i) xr[i] = 0u;
-    float g_s = 1.f, g_z = 0.f, g_zb = 0.f, g_Qb = 0.f, g_Db = 0.f, g_beta = 0.f;
+    float g_s = 1.f, g_z = 0.f, g_zb = 0.f, g_Db = 0.f, g_beta = 0.f;
     double g_Sb = 0.0, g_X = 0.0;
-    uint32_t g_mnmx = 0, g_gidx = 0, g_job = 0, g_t = 0, g_fl = 0;
+    uint32_t g_mnmx = 0, g_gidx = 0, g_meta = 0;  // meta: flags, next update index, tensor
     uint32_t status = kEmpty;
 
     // ---- tile claiming and prefetch (batch layout) ----------------------------------------
@@ -411,16 +422,17 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 
     // Batch version of the advance step, on slot j (fields written by the group's leader).
     auto advance_slot = [&](uint8_t j, float s, float zb, float Qb, float Db, bool sbx) -> uint8_t {
-        const int t = st_t[j];
-        const Advance ad = advance_core<NBITS, G>(t, a.iters, s, zb, Qb, Db, sbx, st_X[j],
-                                                  st_beta[j], tau_min, tau_exp);
+        const uint32_t m = st_b[j].meta;
+        const int t = (int)meta_t(m);
+        const Advance ad = advance_core<NBITS, G>(t, a.iters, s, zb, Qb, Db, sbx, st_c[j].X,
+                                                  st_b[j].beta, tau_min, tau_exp);
         if (bleader) {
-            if (ad.out == kDone) st_zb[j] = ad.zn;
-            else if (ad.out == kNeedShrink) st_fl[j] = (uint8_t)((sbx ? kSbExact : 0) | (kShrink << 1));
+            if (ad.out == kDone) st_a[j].zb = ad.zn;
+            else if (ad.out == kNeedShrink) st_b[j].meta = with_fl(m, (sbx ? kSbExact : 0) | (kShrink << 1));
             else {
-                st_z[j] = ad.zn;
-                st_beta[j] = st_beta[j] * a.kappa;
-                st_t[j] = (uint8_t)(t + 1);
+                st_a[j].z = ad.zn;
+                st_b[j].beta = st_b[j].beta * a.kappa;
+                st_b[j].meta = m + (1u << 8);
             }
         }
         return ad.out;
@@ -429,47 +441,31 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     // Solver state of a group in a slot (read by every lane of the group, written by its
     // first lane) and in the lane's registers.
     struct GroupState {
-        float s, z, zb, Qb, Db, beta;
-        double Sb, X;
-        uint32_t mnmx, gidx, job, t, fl;
+        SlotA a;
+        SlotB b;
+        SlotC c;
     };
-    auto load_state = [&](int j) -> GroupState {
-        return GroupState{st_s[j], st_z[j], st_zb[j], st_Qb[j], st_Db[j], st_beta[j], st_Sb[j],
-                          st_X[j], st_mnmx[j], st_gidx[j], st_job[j], st_t[j], st_fl[j]};
-    };
+    auto load_state = [&](int j) -> GroupState { return GroupState{st_a[j], st_b[j], st_c[j]}; };
     auto put_state = [&](int j, const GroupState &n) {
-        st_s[j] = n.s;
-        st_z[j] = n.z;
-        st_zb[j] = n.zb;
-        st_Qb[j] = n.Qb;
-        st_Db[j] = n.Db;
-        st_beta[j] = n.beta;
-        st_Sb[j] = n.Sb;
-        st_X[j] = n.X;
-        st_mnmx[j] = n.mnmx;
-        st_gidx[j] = n.gidx;
-        st_job[j] = (uint16_t)n.job;
-        st_t[j] = (uint8_t)n.t;
-        st_fl[j] = (uint8_t)n.fl;
+        st_a[j] = n.a;
+        st_b[j] = n.b;
+        st_c[j] = n.c;
     };
     auto cur_state = [&]() -> GroupState {
-        return GroupState{g_s, g_z, g_zb, g_Qb, g_Db, g_beta, g_Sb, g_X, g_mnmx, g_gidx, g_job,
-                          g_t, g_fl};
+        return GroupState{SlotA{g_s, g_z, g_zb, g_Db}, SlotB{g_beta, g_mnmx, g_gidx, g_meta},
+                          SlotC{g_Sb, g_X}};
     };
     auto set_state = [&](const GroupState &n) {
-        g_s = n.s;
-        g_z = n.z;
-        g_zb = n.zb;
-        g_Qb = n.Qb;
-        g_Db = n.Db;
-        g_beta = n.beta;
-        g_Sb = n.Sb;
-        g_X = n.X;
-        g_mnmx = n.mnmx;
-        g_gidx = n.gidx;
-        g_job = n.job;
-        g_t = n.t;
-        g_fl = n.fl;
+        g_s = n.a.s;
+        g_z = n.a.z;
+        g_zb = n.a.zb;
+        g_Db = n.a.Db;
+        g_beta = n.b.beta;
+        g_mnmx = n.b.mnmx;
+        g_gidx = n.b.gidx;
+        g_meta = n.b.meta;
+        g_Sb = n.c.Sb;
+        g_X = n.c.X;
     };
 
     // Per-tensor (min, max) of the binary32 zeros for the 8-bit requantization: a running pair
@@ -501,7 +497,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
         fin_h = (fin_h + n) & RM;
         fin_n -= n;
         uint32_t job = 0;
-        if (valid) job = st_job[j];
+        if (valid) job = meta_job(st_b[j].meta);
         const uint32_t job0 = uniform(job);      // lane 0 always holds a group
         const bool later = valid && job != job0;
         const uint64_t m_later = __ballot(later && bleader);
@@ -512,9 +508,10 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
         float zb = 0.f;
         uint32_t gidx = 0;
         if (valid) {
-            zb = st_zb[j];
-            const float s = st_s[j];
-            gidx = st_gidx[j];
+            const SlotA sa = st_a[j];
+            zb = sa.zb;
+            const float s = sa.s;
+            gidx = st_b[j].gidx;
             const int64_t e0 = (int64_t)gidx * G + sub * EB;   // first weight of this lane
             // Packs this lane's EB codes and stores them, a 16-byte chunk of weights at a
             // time. val(h) maps a weight's binary16 bits to either its exact code or a u whose
@@ -577,7 +574,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             // The accepted evaluation ran in binary32 with the same operations (so its D
             // bounds these codes: none is next to a rounding boundary and none clamps)
             // or in binary64; exact codes only if D was near 1/2.
-            if (st_Db[j] < C::kThr - (float)(1.0 / (1 << (24 - NBITS)))) {
+            if (sa.Db < C::kThr - (float)(1.0 / (1 << (24 - NBITS)))) {
                 emit([&](uint32_t h) { return fmaf(h2f(h), s, zb); });
             } else {
                 emit([&](uint32_t h) {
@@ -590,7 +587,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 if (J.zero16) gbl(J.zero16)[gidx] = f2h(zb);
                 if (J.zero32) gbl(J.zero32)[gidx] = zb;
                 // evaluations run = index of the next update when the group stops
-                if (J.passes) gbl(J.passes)[gidx] = st_t[j];
+                if (J.passes) gbl(J.passes)[gidx] = (uint8_t)meta_t(st_b[j].meta);
             }
         }
         if constexpr (NBITS == 3) {
@@ -757,25 +754,26 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 exq_n -= n;
                 uint8_t out = kDone;
                 if (valid) {
-                    const float s = st_s[j];
-                    const uint8_t fl = st_fl[j];
+                    const SlotA sa = st_a[j];
+                    const float s = sa.s;
+                    const uint32_t m = st_b[j].meta;
+                    const uint32_t fl = meta_fl(m);
                     const int c0 = sub * (EB / 8);
                     if (((fl >> 1) & 3) == kDecide) {
-                        const float z = st_z[j];
+                        const float z = sa.z;
                         const Exact xn = eval_exact<NBITS, G>(xs, j, c0, s, z);
                         const double S = addd_k<KB>(xn.S);
                         const float Q = (float)addd_k<KB>(xn.Q);
                         const float D = maxf_k<KB>((float)xn.D);
-                        double Sb = st_Sb[j];
+                        double Sb = st_c[j].Sb;
                         if (!(fl & kFirst) && !(fl & kSbExact))
-                            Sb = addd_k<KB>(eval_exact<NBITS, G>(xs, j, c0, s, st_zb[j]).S);
+                            Sb = addd_k<KB>(eval_exact<NBITS, G>(xs, j, c0, s, sa.zb).S);
                         if ((fl & kFirst) || !a.early_stop || S <= Sb) {
                             if (bleader) {
-                                st_zb[j] = z;
-                                st_Sb[j] = S;
-                                st_Qb[j] = Q;
-                                st_Db[j] = D;
-                                st_fl[j] = kSbExact;
+                                st_a[j].zb = z;
+                                st_a[j].Db = D;
+                                st_c[j].Sb = S;
+                                st_b[j].meta = with_fl(m, kSbExact);
                             }
                             out = advance_slot(j, s, z, Q, D, true);
                         } else {
@@ -784,8 +782,8 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                     } else {
                         // zero update with the shrink live: z = mean(q - (x - W_e)*s), W_e from
                         // the residual r = x - W_r = (u - q)/s of the accepted iterate.
-                        const double sd = s, zd = st_zb[j], qm = C::QMAX;
-                        const double beta = st_beta[j];
+                        const double sd = s, zd = sa.zb, qm = C::QMAX;
+                        const double beta = st_b[j].beta;
                         double acc = 0.0;
 #pragma unroll 1
                         for (int i = 0; i < EB; ++i) {
@@ -797,10 +795,9 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                         }
                         acc = addd_k<KB>(acc);
                         if (bleader) {
-                            st_z[j] = (float)(acc * (1.0 / G));
-                            st_beta[j] = st_beta[j] * a.kappa;
-                            st_t[j] = (uint8_t)(st_t[j] + 1);
-                            st_fl[j] = fl & kSbExact;
+                            st_a[j].z = (float)(acc * (1.0 / G));
+                            st_b[j].beta = (float)beta * a.kappa;
+                            st_b[j].meta = with_fl(m + (1u << 8), fl & kSbExact);
                         }
                         out = kNext;
                     }
@@ -822,7 +819,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                     const float ulo = fmaf(h2f(g_mnmx & 0xffffu), g_s, g_z);
                     const float uhi = fmaf(h2f(g_mnmx >> 16), g_s, g_z);
                     if (!(ulo >= -0.5f && uhi < C::QMAX + 0.5f)) {
-                        g_fl = (g_fl & (kSbExact | kFirst)) | (kDecide << 1);
+                        g_meta = with_fl(g_meta, (meta_fl(g_meta) & (kSbExact | kFirst)) | (kDecide << 1));
                         status = kHoldExq;
                     }
                 }
@@ -835,11 +832,12 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                         D = maxf_k<2>(D);
                     }
                     const float Q = (float)rint(fma((double)G, (double)g_z, g_X) - (double)T);
-                    const bool first = g_fl & kFirst;
+                    const uint32_t fl = meta_fl(g_meta);
+                    const bool first = fl & kFirst;
                     bool accept = false;
                     uint32_t next = kActive;
                     if (D >= C::kThr) {
-                        g_fl = (g_fl & (kSbExact | kFirst)) | (kDecide << 1);
+                        g_meta = with_fl(g_meta, (fl & (kSbExact | kFirst)) | (kDecide << 1));
                         next = kHoldExq;
                     } else if (first || !a.early_stop) {
                         accept = true;
@@ -849,34 +847,33 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                         // comparison itself.
                         const float Sb = (float)g_Sb;
                         const float m = (float)C::kElemErr + S * 0x1p-18f +
-                                        ((g_fl & kSbExact) ? 0x1p-18f * Sb
+                                        ((fl & kSbExact) ? 0x1p-18f * Sb
                                                            : 4.0f * (float)C::kElemErr + Sb * 0x1p-18f);
                         if (S > Sb + m) next = kHoldFin;
                         else if (S < Sb - m) accept = true;
                         else {
-                            g_fl = (g_fl & kSbExact) | (kDecide << 1);
+                            g_meta = with_fl(g_meta, (fl & kSbExact) | (kDecide << 1));
                             next = kHoldExq;
                         }
                     }
                     if (accept) {
                         g_zb = g_z;
                         g_Sb = S;
-                        g_Qb = Q;
                         g_Db = D;
-                        g_fl = 0;
-                        const Advance ad = advance_core<NBITS, G>((int)g_t, a.iters, g_s, g_z, Q, D,
+                        g_meta = with_fl(g_meta, 0);
+                        const Advance ad = advance_core<NBITS, G>((int)meta_t(g_meta), a.iters, g_s, g_z, Q, D,
                                                                   false, g_X, g_beta, tau_min,
                                                                   tau_exp);
                         if (ad.out == kDone) {
                             g_zb = ad.zn;
                             next = kHoldFin;
                         } else if (ad.out == kNeedShrink) {
-                            g_fl = kShrink << 1;
+                            g_meta = with_fl(g_meta, kShrink << 1);
                             next = kHoldExq;
                         } else {
                             g_z = ad.zn;
                             g_beta = g_beta * a.kappa;
-                            g_t = g_t + 1;
+                            g_meta = g_meta + (1u << 8);
                         }
                     }
                     status = next;
@@ -929,21 +926,12 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 sxs = fma((double)h2f(i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu), sd, sxs);
             sxs = addd_k<KB>(sxs);
             if (bleader) {
-                st_z[j] = z0;
-                st_zb[j] = z0;
-                st_s[j] = s;
+                st_a[j] = SlotA{s, z0, z0, 0.f};
                 float beta0 = a.beta0;
                 asm volatile("" : "+s"(beta0));     // kept in a scalar register until here
-                st_beta[j] = beta0;
-                st_Qb[j] = 0.f;
-                st_Db[j] = 0.f;
-                st_Sb[j] = 0.0;
-                st_X[j] = sxs;
-                st_mnmx[j] = (uint32_t)f2h(mn) | ((uint32_t)f2h(mx) << 16);
-                st_gidx[j] = (uint32_t)(pf_g0 + k);
-                st_job[j] = (uint16_t)pf_job;
-                st_t[j] = 1;
-                st_fl[j] = kFirst;
+                st_b[j] = SlotB{beta0, (uint32_t)f2h(mn) | ((uint32_t)f2h(mx) << 16),
+                                (uint32_t)(pf_g0 + k), (uint32_t)pf_job << 16 | 1u << 8 | kFirst};
+                st_c[j] = SlotC{0.0, sxs};
             }
         }
         push_batch(valid, kNext, j);
