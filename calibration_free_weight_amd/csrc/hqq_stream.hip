@@ -641,7 +641,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 
     // The outer loop takes one prefetched tile in per turn (INIT); the inner loop does all
     // other work. Only the outer loop touches the prefetch registers, so they keep one place.
-    bool done = false;
+    bool done = false, epi_first = false;
     while (!done) {
         while (true) {
             if (--budget <= 0) {
@@ -740,6 +740,12 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             const bool idle = n_act == 0;            // no pass possible now
 
             if (fin_n >= GB || (fin_n > 0 && idle && !can_init && rdy_n == 0 && exq_n == 0)) {
+                // When a tile is wanted as well, the epilogue runs in the outer loop after the
+                // tile's wait and frees the slots the tile takes.
+                if (pf_ok && fin_n >= GB && (rdy_n < n_empty + n_hold || idle)) {
+                    epi_first = true;
+                    break;
+                }
                 epilogue();
                 continue;
             }
@@ -885,6 +891,16 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             break;
         }
         if (done) break;
+        // Loads and stores share one completion counter, retired in order: a wait for the
+        // tile issued after an epilogue's stores would wait for those too. So the tile is
+        // waited for here, before any store of this turn, and INIT itself waits for nothing.
+#pragma unroll
+        for (int i = 0; i < EB / 8; ++i) asm volatile("" : "+v"(pf[i]));
+        if (epi_first) {
+            epi_first = false;
+            epilogue();
+            if (fre_n < GB) continue;            // finished groups of a later tensor stayed
+        }
         // ================= INIT: a prefetched tile becomes ready groups ===============
         budget += 8 * (int64_t)(a.iters + 4) * GB;
         const int nv = pf_nv;
