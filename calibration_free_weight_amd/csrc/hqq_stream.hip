@@ -488,6 +488,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 
     // ================= EPILOGUE: codes, packing, scale / zero of up to GB finished groups
     auto epilogue = [&]() {
+        __builtin_amdgcn_s_setprio(0);
         // One tensor per batch (descriptor in scalar registers); groups of another tensor
         // go back to the finished list for a later batch.
         const int n = fin_n < GB ? (int)fin_n : GB;
@@ -644,6 +645,11 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     bool done = false, epi_first = false;
     while (!done) {
         while (true) {
+            // Wave priority: the step choice and SWAP are short chains of LDS round trips
+            // that decide what a wave does next; raised, they issue as soon as their data
+            // returns, while the arithmetic phases (PASS, EXACT, EPILOGUE, INIT) of the
+            // SIMD's other waves fill the gaps. Measured 1-5 % faster than one level.
+            __builtin_amdgcn_s_setprio(1);
             if (--budget <= 0) {
                 done = true;
                 break;
@@ -752,6 +758,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 
             if (exq_n >= GB || (exq_n > 0 && idle && rdy_n == 0)) {
                 // ================= EXACT: binary64 decisions and shrink updates ==============
+                __builtin_amdgcn_s_setprio(0);
                 const int n = exq_n < GB ? (int)exq_n : GB;
                 const bool valid = k < n;
                 uint8_t j = 0;
@@ -829,6 +836,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                         status = kHoldExq;
                     }
                 }
+                __builtin_amdgcn_s_setprio(0);
                 if (status == kActive) {
                     float S, T, D;
                     eval_fast<NBITS, WP>(xr, g_s, g_z, S, T, D);
@@ -902,6 +910,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             if (fre_n < GB) continue;            // finished groups of a later tensor stayed
         }
         // ================= INIT: a prefetched tile becomes ready groups ===============
+        __builtin_amdgcn_s_setprio(0);
         budget += 8 * (int64_t)(a.iters + 4) * GB;
         const int nv = pf_nv;
         const bool valid = k < nv;
