@@ -271,38 +271,76 @@ void hqo_solve_groups(const uint16_t *w, int64_t n_groups, int g, int nbits, flo
     }
 }
 
-/* Zero-point storage.
- * 16-bit: zero = binary16(z).
- * 8-bit [TR "Benchmark results / Llama-2": the zero-point goes to 8 bit with no extra
- * grouping and no optimisation]. Reading: one min-max affine uint8 round-to-nearest
- * quantizer over all zeros of the tensor, on the grid its stored binary16 pair defines:
- *   step = binary16((zmax - zmin) / 255)   (1 if that is 0: all zeros equal),
- *   base = binary16(zmin),
- *   zq   = clamp(round-half-even((z - base) / step), 0, 255)   (binary32 operations),
- * meta = {step, base}; the stored zero reads back as zq * step + base. Quantizing against the
- * stored pair (not the unrounded one) keeps the read-back within half a step. */
-void hqo_zero_requant(const float *z, int64_t n, uint8_t *zq, uint16_t *meta)
+/* One min-max affine uint8 round-to-nearest quantizer over n binary32 values, on the grid
+ * of its stored binary16 pair (the rule of both 8-bit zeros and 8-bit scales below):
+ *   step = binary16((vmax - vmin) / 255)   (1 if that is 0: all values equal),
+ *   base = binary16(vmin),
+ *   q    = clamp(round-half-even((v - base) / step), 0, 255)   (binary32 operations),
+ * meta = {step, base}; a value reads back as q * step + base. Quantizing against the stored
+ * pair (not the unrounded one) keeps the read-back within half a step. */
+void hqo_u8_affine(const float *v, int64_t n, uint8_t *q, uint16_t *meta)
 {
-    float zmin = z[0], zmax = z[0];
+    float vmin = v[0], vmax = v[0];
     for (int64_t i = 1; i < n; ++i) {
-        zmin = fminf(zmin, z[i]);
-        zmax = fmaxf(zmax, z[i]);
+        vmin = fminf(vmin, v[i]);
+        vmax = fmaxf(vmax, v[i]);
     }
-    uint16_t h_step = hqo_float_to_half((zmax - zmin) / 255.0f);
+    uint16_t h_step = hqo_float_to_half((vmax - vmin) / 255.0f);
     float step = hqo_half_to_float(h_step);
     if (!(step > 0.0f)) {
         h_step = 0x3c00;                            /* binary16 1.0 */
         step = 1.0f;
     }
-    uint16_t h_base = hqo_float_to_half(zmin);
+    uint16_t h_base = hqo_float_to_half(vmin);
     float base = hqo_half_to_float(h_base);
     for (int64_t i = 0; i < n; ++i) {
-        float v = nearbyintf((z[i] - base) / step);
-        v = fminf(fmaxf(v, 0.0f), 255.0f);
-        zq[i] = (uint8_t)v;
+        float c = nearbyintf((v[i] - base) / step);
+        c = fminf(fmaxf(c, 0.0f), 255.0f);
+        q[i] = (uint8_t)c;
     }
     meta[0] = h_step;
     meta[1] = h_base;
+}
+
+/* Zero-point storage.
+ * 16-bit: zero = binary16(z).
+ * 8-bit [TR "Benchmark results / Llama-2": the zero-point goes to 8 bit with no extra
+ * grouping and no optimisation]. Reading: one hqo_u8_affine quantizer over all zeros of the
+ * tensor; meta = {step, base}. */
+void hqo_zero_requant(const float *z, int64_t n, uint8_t *zq, uint16_t *meta)
+{
+    hqo_u8_affine(z, n, zq, meta);
+}
+
+/* 8-bit scales [TR "Benchmark results / Llama-2", the note on the HQQ_g16_s row of the
+ * Llama-2 table: the scale is quantized to 8 bit as well, with a group size of 128].
+ * Reading: the stored binary16 scales of a tensor (one per weight group, in group order)
+ * are cut into consecutive groups of `group` values, the last one shorter when group does
+ * not divide n; each gets its own hqo_u8_affine quantizer, like the zero-point ("without
+ * optimisation"), and meta[2m], meta[2m+1] = {step, base} of group m. The codes of the
+ * weights are not re-derived with the quantized scale. */
+void hqo_scale_requant(const uint16_t *scale, int64_t n, int group, uint8_t *sq, uint16_t *meta)
+{
+    float v[4096];
+    assert(group >= 1 && group <= 4096);
+    for (int64_t g0 = 0, m = 0; g0 < n; g0 += group, ++m) {
+        int64_t len = n - g0 < group ? n - g0 : group;
+        for (int64_t i = 0; i < len; ++i) v[i] = hqo_half_to_float(scale[g0 + i]);
+        hqo_u8_affine(v, len, sq + g0, meta + 2 * m);
+    }
+}
+
+/* Read-back of 8-bit scales as binary16 scales for reconstruction: one binary32 fused
+ * multiply-add q * step + base, rounded to binary16. */
+void hqo_scale_dequant(const uint8_t *sq, const uint16_t *meta, int64_t n, int group,
+                       uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t m = i / group;
+        float step = hqo_half_to_float(meta[2 * m]);
+        float base = hqo_half_to_float(meta[2 * m + 1]);
+        out[i] = hqo_float_to_half(fmaf((float)sq[i], step, base));
+    }
 }
 
 void hqo_zero_to_half(const float *z, int64_t n, uint16_t *zh)

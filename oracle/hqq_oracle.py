@@ -74,6 +74,12 @@ class Oracle:
                                        _vp, _vp, _vp, _vp]
         L.hqo_zero_requant.restype = None
         L.hqo_zero_requant.argtypes = [_f32p, C.c_int64, _u8p, _u16p]
+        L.hqo_u8_affine.restype = None
+        L.hqo_u8_affine.argtypes = [_f32p, C.c_int64, _u8p, _u16p]
+        L.hqo_scale_requant.restype = None
+        L.hqo_scale_requant.argtypes = [_u16p, C.c_int64, C.c_int, _u8p, _u16p]
+        L.hqo_scale_dequant.restype = None
+        L.hqo_scale_dequant.argtypes = [_u8p, _u16p, C.c_int64, C.c_int, _u16p]
         L.hqo_zero_to_half.restype = None
         L.hqo_zero_to_half.argtypes = [_f32p, C.c_int64, _u16p]
         L.hqo_packed_bytes.restype = C.c_size_t
@@ -169,6 +175,33 @@ class Oracle:
         meta = np.empty(2, np.uint16)
         self.L.hqo_zero_requant(z, z.size, zq, meta)
         return zq, meta
+
+    def u8_affine(self, v):
+        """One min-max affine uint8 quantizer over all of v: (codes, meta {step, base})."""
+        v = np.ascontiguousarray(v, np.float32).reshape(-1)
+        q = np.empty(v.size, np.uint8)
+        meta = np.empty(2, np.uint16)
+        self.L.hqo_u8_affine(v, v.size, q, meta)
+        return q, meta
+
+    def scale_requant(self, scale16, group=128):
+        """8-bit scales: binary16 scales (uint16 bits) -> (codes, meta [2*groups])."""
+        scale16 = np.ascontiguousarray(scale16, np.uint16).reshape(-1)
+        n = scale16.size
+        sq = np.empty(n, np.uint8)
+        meta = np.empty(2 * ((n + group - 1) // group), np.uint16)
+        if n:
+            self.L.hqo_scale_requant(scale16, n, group, sq, meta)
+        return sq, meta
+
+    def scale_dequant(self, sq, meta, group=128):
+        """binary16 scales (uint16 bits) read back from 8-bit scales."""
+        sq = np.ascontiguousarray(sq, np.uint8).reshape(-1)
+        meta = np.ascontiguousarray(meta, np.uint16).reshape(-1)
+        out = np.empty(sq.size, np.uint16)
+        if sq.size:
+            self.L.hqo_scale_dequant(sq, meta, sq.size, group, out)
+        return out
 
     def zero_to_half(self, z):
         z = np.ascontiguousarray(z, np.float32).reshape(-1)
