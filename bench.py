@@ -118,6 +118,46 @@ def cpu_baseline(specs, weights, seconds):
                        f"{total_t:.1f} s; full quantize incl. zero storage and packing")
 
 
+def scale8_row(dev, stream, reps=10):
+    """8-bit scales in runs of 128 (the pages' HQQ_g16_s variant) on the scale array of a
+    2-bit g16 Llama-2-7B-shaped stack: requant and read-back, each timed with HIP events on
+    the launch stream over `reps` launches. Both are HBM-bound; algorithmic bytes per scale:
+    requant 2 read + 1 written, read-back 1 read + 2 written, plus 4 per run of 128 (meta)."""
+    import torch
+    import synth
+    from calibration_free_weight_amd import hqq
+    n, group = 6_476_005_376 // 16, 128
+    n_runs = (n + group - 1) // group
+    v = synth.scale_values(n, 4711, device=dev)
+    sq = torch.empty(n, dtype=torch.uint8, device=dev)
+    meta = torch.empty(2 * n_runs, dtype=torch.float16, device=dev)
+    back = torch.empty(n, dtype=torch.float16, device=dev)
+    calls = {
+        "requant": (lambda: hqq.hqq_requant_scales(v, n, group, sq, meta, stream.cuda_stream),
+                    3 * n + 4 * n_runs, "scale_requant_kernel<16>"),
+        "dequant": (lambda: hqq.hqq_dequantize_scales(sq, meta, n, group, back,
+                                                      stream.cuda_stream),
+                    3 * n + 4 * n_runs, "scale_dequant_kernel"),
+    }
+    row = {"variant": "8-bit scales, runs of 128 (HQQ_g16_s)", "n_scales": n, "bound": "hbm"}
+    for name, (fn, nbytes, kern) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        row[name] = {"kernel": kern, "launch_ms": round(ms, 4), "bytes_per_launch": nbytes,
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del v, sq, meta, back
+    return row
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +296,8 @@ def main():
                      "mean_passes": round(mean_passes, 4),
                      "hbm": hbm, "alu": alu},
     }
+    log("bench: 8-bit scales")
+    result["next_rows"] = {"scale8": scale8_row(dev, stream)}
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(specs, weights, args.cpu_seconds)

@@ -354,6 +354,51 @@ hqq_status hqq_dequantize(const void *packed, const void *scale, const void *zer
     return HQQ_OK;
 }
 
+static hqq_status check_scale_group(int scale_group)
+{
+    if (scale_group < 8 || scale_group > 512 || (scale_group & (scale_group - 1)) != 0)
+        return fail(HQQ_ERR_ARG, "scale_group must be a power of two in [8, 512]");
+    return HQQ_OK;
+}
+
+hqq_status hqq_requant_scales(const void *scale, int64_t n, int scale_group, uint8_t *scale_q,
+                              void *scale_meta, void *stream)
+{
+    if (n < 0) return fail(HQQ_ERR_ARG, "n must be >= 0");
+    hqq_status st = check_scale_group(scale_group);
+    if (st != HQQ_OK) return st;
+    if (n == 0) return HQQ_OK;
+    if (!scale || !scale_q || !scale_meta)
+        return fail(HQQ_ERR_ARG, "scale, scale_q and scale_meta must be non-null");
+    if (!aligned(scale, 16) || !aligned(scale_q, 8) || !aligned(scale_meta, 4))
+        return fail(HQQ_ERR_ARG, "scale must be 16-, scale_q 8- and scale_meta 4-byte aligned");
+    hipError_t e = hqq::launch_scale_requant(static_cast<const uint16_t *>(scale), n, scale_group,
+                                             scale_q, static_cast<uint16_t *>(scale_meta),
+                                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "scale requant launch");
+    g_last_error.clear();
+    return HQQ_OK;
+}
+
+hqq_status hqq_dequantize_scales(const uint8_t *scale_q, const void *scale_meta, int64_t n,
+                                 int scale_group, void *scale_out, void *stream)
+{
+    if (n < 0) return fail(HQQ_ERR_ARG, "n must be >= 0");
+    hqq_status st = check_scale_group(scale_group);
+    if (st != HQQ_OK) return st;
+    if (n == 0) return HQQ_OK;
+    if (!scale_q || !scale_meta || !scale_out)
+        return fail(HQQ_ERR_ARG, "scale_q, scale_meta and scale_out must be non-null");
+    if (!aligned(scale_q, 8) || !aligned(scale_meta, 4) || !aligned(scale_out, 16))
+        return fail(HQQ_ERR_ARG, "scale_q must be 8-, scale_meta 4- and scale_out 16-byte aligned");
+    hipError_t e = hqq::launch_scale_dequant(scale_q, static_cast<const uint16_t *>(scale_meta), n,
+                                             scale_group, static_cast<uint16_t *>(scale_out),
+                                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "scale dequantize launch");
+    g_last_error.clear();
+    return HQQ_OK;
+}
+
 hqq_status hqq_pack(const uint8_t *codes, int64_t n_codes, int nbits, void *packed, void *stream)
 {
     if (!valid_bits(nbits)) return fail(HQQ_ERR_ARG, "nbits must be 1, 2, 3, 4 or 8");

@@ -168,6 +168,156 @@ __global__ void __launch_bounds__(256) unpack_kernel(const uint8_t *packed, int6
         codes[k] = (uint8_t)get_code(packed, k, nbits);
 }
 
+// ---------------------------------------------------------------------------------------
+// 8-bit scales [techreport.ngo, "Half-Quadratic Quantization of Large Machine Learning
+// Models", section "Benchmark results / Llama-2", note on the HQQ_g16_s row: that
+// variant also stores its scales on 8-bit grids, one per 128 scales]. Each run of SG consecutive binary16
+// scales gets the min-max affine uint8 rule of the 8-bit zero-point:
+//   step = binary16((vmax - vmin)/255) (1 if that is 0), base = binary16(vmin),
+//   q = clamp(rne((v - base)/step), 0, 255), meta[2m..2m+1] = {step, base} of run m.
+// A lane holds 8 consecutive scales (one 16-byte load), so LPG = SG/8 neighbouring lanes
+// of one wave hold a run and reduce its min / max with LPG-wide butterflies. HBM-bound: it
+// reads 2 B and writes 1 B per scale plus 4 B per run.
+// ---------------------------------------------------------------------------------------
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+constexpr int kScaleUnroll = 4;                 // 512-scale tiles in flight per wave
+
+template <int LPG>
+__global__ void __launch_bounds__(256) scale_requant_kernel(const uint16_t *__restrict__ scale,
+                                                            int64_t n, uint8_t *__restrict__ sq,
+                                                            uint16_t *__restrict__ meta)
+{
+    constexpr int SG = 8 * LPG, U = kScaleUnroll;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+    const int64_t n_waves = (int64_t)gridDim.x * 4;
+    // The loop bound is per wave: every lane of a wave runs the butterflies together.
+    for (int64_t t0 = wave * U; t0 * 512 < n; t0 += n_waves * U) {
+        v4u w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {           // all loads first
+            const int64_t e0 = ((t0 + u) * 64 + lane) * 8;
+            if (e0 + 8 <= n) {
+                w[u] = *reinterpret_cast<const v4u *>(scale + e0);
+            } else {                            // a ragged end: absent scales read as NaN
+                uint32_t h[4] = {0x7e007e00u, 0x7e007e00u, 0x7e007e00u, 0x7e007e00u};
+                for (int i = 0; i < 8 && e0 + i < n; ++i)
+                    h[i >> 1] = (h[i >> 1] & (i & 1 ? 0x0000ffffu : 0xffff0000u)) |
+                                (uint32_t)scale[e0 + i] << (16 * (i & 1));
+                w[u] = v4u{h[0], h[1], h[2], h[3]};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e0 = ((t0 + u) * 64 + lane) * 8;
+            const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = h2f((uint16_t)(i & 1 ? ws[i >> 1] >> 16 : ws[i >> 1]));
+            float vmin = INFINITY, vmax = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {      // fminf / fmaxf skip the NaN of absent scales
+                vmin = fminf(vmin, v[i]);
+                vmax = fmaxf(vmax, v[i]);
+            }
+#pragma unroll
+            for (int off = LPG / 2; off >= 1; off /= 2) {
+                vmin = fminf(vmin, __shfl_xor(vmin, off));
+                vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+            }
+            if (e0 >= n) continue;              // no scale here (the butterflies are done)
+            uint16_t h_step = f2h((vmax - vmin) / 255.0f);
+            float step = h2f(h_step);
+            if (!(step > 0.0f)) {
+                h_step = 0x3c00;                // binary16 1.0
+                step = 1.0f;
+            }
+            const uint16_t h_base = f2h(vmin);
+            const float base = h2f(h_base);
+            // The code is rne of the binary32 quotient (v - base)/step, clamped to [0, 255].
+            // Quotient by the correctly rounded reciprocal and one fused correction: within a
+            // few ulps of the binary32 quotient (x >= 0, step a normal binary32 number, no
+            // overflow), so both round to the same integer unless the quotient is within
+            // 2^-14 (at least 4 ulps below 256) of a half-integer; those take the division.
+            const float rcp = 1.0f / step;
+            float q[8];
+            bool near = false;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float x = v[i] - base;
+                const float q0 = x * rcp;
+                q[i] = fmaf(fmaf(-q0, step, x), rcp, q0);
+                near |= fabsf(fabsf(q[i] - rintf(q[i])) - 0.5f) <= 0x1p-14f;
+            }
+            if (near) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) q[i] = (v[i] - base) / step;
+            }
+            // v_cvt_pk_u8_f32: round half to even, saturate to [0, 255]
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lo = __builtin_amdgcn_cvt_pk_u8_f32(q[i], i, lo);
+                hi = __builtin_amdgcn_cvt_pk_u8_f32(q[i + 4], i, hi);
+            }
+            if (e0 + 8 <= n) {
+                *reinterpret_cast<v2u *>(sq + e0) = v2u{lo, hi};
+            } else {
+                for (int i = 0; i < 8 && e0 + i < n; ++i)
+                    sq[e0 + i] = (uint8_t)((i < 4 ? lo : hi) >> (8 * (i & 3)));
+            }
+            if (lane % LPG == 0)
+                reinterpret_cast<uint32_t *>(meta)[e0 / SG] =
+                    (uint32_t)h_step | (uint32_t)h_base << 16;
+        }
+    }
+}
+
+// Read-back of 8-bit scales: binary16(fma(q, step, base)) in binary32, 8 scales per lane,
+// kScaleUnroll chunks in flight per thread.
+__global__ void __launch_bounds__(256) scale_dequant_kernel(const uint8_t *__restrict__ sq,
+                                                            const uint16_t *__restrict__ meta,
+                                                            int64_t n, int sg_log2,
+                                                            uint16_t *__restrict__ out)
+{
+    constexpr int U = kScaleUnroll;
+    const int64_t T = (int64_t)gridDim.x * 256;
+    for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 * 8 < n; c0 += T * U) {
+        v2u w[U];
+        uint32_t mm[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e0 = (c0 + u * T) * 8;
+            w[u] = v2u{0u, 0u};
+            mm[u] = 0;
+            if (e0 + 8 <= n) w[u] = *reinterpret_cast<const v2u *>(sq + e0);
+            if (e0 < n) mm[u] = reinterpret_cast<const uint32_t *>(meta)[e0 >> sg_log2];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t e0 = (c0 + u * T) * 8;
+            if (e0 >= n) break;
+            const float step = h2f((uint16_t)mm[u]), base = h2f((uint16_t)(mm[u] >> 16));
+            if (e0 + 8 <= n) {
+                uint32_t o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t b = i < 2 ? w[u].x : w[u].y;
+                    const int sh = 16 * (i & 1);
+                    o[i] = (uint32_t)f2h(fmaf((float)((b >> sh) & 0xffu), step, base)) |
+                           (uint32_t)f2h(fmaf((float)((b >> (sh + 8)) & 0xffu), step, base)) << 16;
+                }
+                *reinterpret_cast<v4u *>(out + e0) = v4u{o[0], o[1], o[2], o[3]};
+            } else {
+                for (int i = 0; i < 8 && e0 + i < n; ++i)
+                    out[e0 + i] = f2h(fmaf((float)sq[e0 + i], step, base));
+            }
+        }
+    }
+}
+
 unsigned grid_for(int64_t items, int per_block)
 {
     int64_t b = (items + per_block - 1) / per_block;
@@ -214,6 +364,35 @@ hipError_t launch_unpack(const uint8_t *packed, int64_t n, int nbits, uint8_t *c
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(n, 256)), dim3(256), 0, stream, packed, n,
                        nbits, codes);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_requant(const uint16_t *scale, int64_t n, int scale_group, uint8_t *sq,
+                                uint16_t *meta, hipStream_t stream)
+{
+    if (n == 0) return hipSuccess;
+    const dim3 grid(grid_for((n + 511) / 512 / kScaleUnroll * 64, 256)), block(256);
+    switch (scale_group) {
+    case 8: hipLaunchKernelGGL(scale_requant_kernel<1>, grid, block, 0, stream, scale, n, sq, meta); break;
+    case 16: hipLaunchKernelGGL(scale_requant_kernel<2>, grid, block, 0, stream, scale, n, sq, meta); break;
+    case 32: hipLaunchKernelGGL(scale_requant_kernel<4>, grid, block, 0, stream, scale, n, sq, meta); break;
+    case 64: hipLaunchKernelGGL(scale_requant_kernel<8>, grid, block, 0, stream, scale, n, sq, meta); break;
+    case 128: hipLaunchKernelGGL(scale_requant_kernel<16>, grid, block, 0, stream, scale, n, sq, meta); break;
+    case 256: hipLaunchKernelGGL(scale_requant_kernel<32>, grid, block, 0, stream, scale, n, sq, meta); break;
+    case 512: hipLaunchKernelGGL(scale_requant_kernel<64>, grid, block, 0, stream, scale, n, sq, meta); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_dequant(const uint8_t *sq, const uint16_t *meta, int64_t n,
+                                int scale_group, uint16_t *out, hipStream_t stream)
+{
+    if (n == 0) return hipSuccess;
+    int lg = 0;
+    while ((1 << lg) < scale_group) ++lg;
+    hipLaunchKernelGGL(scale_dequant_kernel, dim3(grid_for((n + 7) / 8 / kScaleUnroll, 256)), dim3(256), 0,
+                       stream, sq, meta, n, lg, out);
     return hipGetLastError();
 }
 

@@ -57,6 +57,12 @@ hipError_t launch_dequant(const uint8_t *packed, const uint16_t *scale, const vo
                           const uint16_t *meta, int64_t n, int nbits, int g, int zero_bits,
                           uint16_t *out, hipStream_t stream);
 
+// 8-bit scales: scale_group a power of two in [8, 512]; buffers 16-byte aligned (meta 4).
+hipError_t launch_scale_requant(const uint16_t *scale, int64_t n, int scale_group, uint8_t *sq,
+                                uint16_t *meta, hipStream_t stream);
+hipError_t launch_scale_dequant(const uint8_t *sq, const uint16_t *meta, int64_t n,
+                                int scale_group, uint16_t *out, hipStream_t stream);
+
 hipError_t launch_pack(const uint8_t *codes, int64_t n, int nbits, uint8_t *packed,
                        hipStream_t stream);
 

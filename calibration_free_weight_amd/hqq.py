@@ -17,8 +17,9 @@ HQQ_OK, HQQ_ERR_ARG, HQQ_ERR_UNSUPPORTED, HQQ_ERR_WORKSPACE, HQQ_ERR_DEVICE = ra
 
 # Functions declared in include/hqq.h (checked by the tests against the header).
 EXPORTS = ("hqq_packed_bytes", "hqq_workspace_bytes", "hqq_quantize", "hqq_quantize_batch",
-           "hqq_solve_batch", "hqq_requant_batch", "hqq_dequantize", "hqq_pack", "hqq_unpack",
-           "hqq_status_string", "hqq_last_error")
+           "hqq_solve_batch", "hqq_requant_batch", "hqq_dequantize", "hqq_requant_scales",
+           "hqq_dequantize_scales", "hqq_pack", "hqq_unpack", "hqq_status_string",
+           "hqq_last_error")
 
 
 class HQQError(RuntimeError):
@@ -59,6 +60,10 @@ def lib():
             getattr(L, name).argtypes = [C.POINTER(hqq_job), i32, vp, C.c_size_t, vp]
         L.hqq_dequantize.restype = i32
         L.hqq_dequantize.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp]
+        L.hqq_requant_scales.restype = i32
+        L.hqq_requant_scales.argtypes = [vp, i64, i32, vp, vp, vp]
+        L.hqq_dequantize_scales.restype = i32
+        L.hqq_dequantize_scales.argtypes = [vp, vp, i64, i32, vp, vp]
         L.hqq_pack.restype = i32
         L.hqq_pack.argtypes = [vp, i64, i32, vp, vp]
         L.hqq_unpack.restype = i32
@@ -150,6 +155,27 @@ def hqq_dequantize(packed, scale, zero, zero_meta, rows, cols, nbits, group_size
     _check(lib().hqq_dequantize(_p(packed), _p(scale), _p(zero), _p(zero_meta), rows, cols,
                                 nbits, group_size, axis, zero_bits, _p(W_out),
                                 _stream(stream)))
+
+
+def hqq_requant_scales(scale, n, scale_group, scale_q, scale_meta, stream=None) -> None:
+    _check(lib().hqq_requant_scales(_p(scale), n, scale_group, _p(scale_q), _p(scale_meta),
+                                    _stream(stream)))
+
+
+def hqq_dequantize_scales(scale_q, scale_meta, n, scale_group, scale_out, stream=None) -> None:
+    _check(lib().hqq_dequantize_scales(_p(scale_q), _p(scale_meta), n, scale_group,
+                                       _p(scale_out), _stream(stream)))
+
+
+def requant_scales(scale, scale_group=128, stream=None):
+    """Allocate and fill 8-bit scales for a binary16 scale tensor: (scale_q, scale_meta)."""
+    import torch
+    n = scale.numel()
+    sq = torch.empty(max(n, 1), dtype=torch.uint8, device=scale.device)
+    meta = torch.empty(max(2 * ((n + scale_group - 1) // scale_group), 2), dtype=torch.float16,
+                       device=scale.device)
+    hqq_requant_scales(scale, n, scale_group, sq, meta, stream)
+    return sq[:n], meta[:2 * ((n + scale_group - 1) // scale_group)]
 
 
 def hqq_pack(codes, n_codes, nbits, packed, stream=None) -> None:

@@ -124,6 +124,26 @@ hqq_status hqq_dequantize(const void *packed, const void *scale, const void *zer
                           const void *zero_meta, int64_t rows, int64_t cols, int nbits,
                           int group_size, int axis, int zero_bits, void *W_out, void *stream);
 
+/* 8-bit scales [TR "Benchmark results / Llama-2", the note on the HQQ_g16_s row: that
+ * variant also stores its scales on 8-bit grids, one per 128 scales]. Quantizes n binary16 scales (e.g. the `scale`
+ * output of hqq_quantize, one per weight group, in group order) in runs of `scale_group`
+ * consecutive scales (the last run shorter when scale_group does not divide n). Each run m
+ * gets the min-max affine uint8 rule of 8-bit zeros, with no optimisation:
+ *   step = binary16((vmax - vmin)/255) (1 if that is 0), base = binary16(vmin),
+ *   scale_q[i] = clamp(rne((v_i - base)/step), 0, 255)       (binary32 operations),
+ *   scale_meta[2m] = step, scale_meta[2m + 1] = base.
+ * The weight codes are not re-derived. scale: binary16 [n], 16-byte aligned; scale_q:
+ * uint8 [n], 8-byte aligned; scale_meta: binary16 [2*ceil(n/scale_group)], 4-byte aligned.
+ * scale_group: a power of two in [8, 512] (128 on the pages). n = 0 does nothing. */
+hqq_status hqq_requant_scales(const void *scale, int64_t n, int scale_group, uint8_t *scale_q,
+                              void *scale_meta, void *stream);
+
+/* Read back 8-bit scales as binary16 scales for hqq_dequantize:
+ * scale_out[i] = binary16(fma(scale_q[i], step, base)) with run i/scale_group's pair, the
+ * fma in binary32. Same layouts as hqq_requant_scales; scale_out is 16-byte aligned. */
+hqq_status hqq_dequantize_scales(const uint8_t *scale_q, const void *scale_meta, int64_t n,
+                                 int scale_group, void *scale_out, void *stream);
+
 /* Pack n_codes uint8 codes (each < 2^nbits) into the packed layout above; `packed` must be
  * 16-byte aligned and hold hqq_packed_bytes(n_codes, nbits) bytes. Codes >= 2^nbits are
  * masked to their low nbits bits. */

@@ -313,7 +313,7 @@ void hqo_zero_requant(const float *z, int64_t n, uint8_t *zq, uint16_t *meta)
 }
 
 /* 8-bit scales [TR "Benchmark results / Llama-2", the note on the HQQ_g16_s row of the
- * Llama-2 table: the scale is quantized to 8 bit as well, with a group size of 128].
+ * Llama-2 table: that variant also stores its scales on 8-bit grids, one per 128 scales].
  * Reading: the stored binary16 scales of a tensor (one per weight group, in group order)
  * are cut into consecutive groups of `group` values, the last one shorter when group does
  * not divide n; each gets its own hqo_u8_affine quantizer, like the zero-point ("without

@@ -52,6 +52,22 @@ def student_t_weights(rows: int, cols: int, seed: int, device="cpu",
     return out
 
 
+def scale_values(n: int, seed: int, device="cpu", log_mean: float = -4.6,
+                 log_std: float = 0.4) -> torch.Tensor:
+    """fp16 [n] positive lognormal values shaped like per-group binary16 scales (1/s of
+    2-bit groups of the weights above: around 0.01, a few tens of percent apart)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    out = torch.empty(n, dtype=torch.float16, device=dev)
+    for a in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - a)
+        z = torch.randn(m, generator=gen, device=dev, dtype=torch.float32)
+        out[a:a + m].copy_(z.mul_(log_std).add_(log_mean).exp_().to(torch.float16))
+        del z
+    return out
+
+
 @dataclass(frozen=True)
 class TensorSpec:
     name: str

@@ -106,3 +106,23 @@ def test_other_entry_points_validate(H):
                             4, 64, 4, 64, 1, 8, C.c_void_p(0x4000), None) == H.HQQ_ERR_ARG
     assert L.hqq_dequantize(None, None, None, None, 4, 64, 4, 64, 0, 16, None, None) == \
         H.HQQ_ERR_UNSUPPORTED
+
+
+def test_scale_entry_points_validate(H):
+    L = H.lib()
+    s, q, m, o = (C.c_void_p(a) for a in (0x1000, 0x2000, 0x3000, 0x4000))
+    ok, arg = H.HQQ_OK, H.HQQ_ERR_ARG
+    for g in (7, 4, 1024, 96, 0, -128):                       # not a power of two in [8, 512]
+        assert L.hqq_requant_scales(s, 100, g, q, m, None) == arg
+        assert L.hqq_dequantize_scales(q, m, 100, g, o, None) == arg
+    assert L.hqq_requant_scales(s, -1, 128, q, m, None) == arg
+    assert L.hqq_requant_scales(s, 0, 128, None, None, None) == ok       # empty: nothing to do
+    assert L.hqq_dequantize_scales(None, None, 0, 128, None, None) == ok
+    assert L.hqq_requant_scales(None, 100, 128, q, m, None) == arg
+    assert L.hqq_requant_scales(s, 100, 128, q, None, None) == arg
+    assert L.hqq_requant_scales(C.c_void_p(0x1008), 100, 128, q, m, None) == arg   # scale 16 B
+    assert L.hqq_requant_scales(s, 100, 128, C.c_void_p(0x2004), m, None) == arg   # scale_q 8 B
+    assert L.hqq_requant_scales(s, 100, 128, q, C.c_void_p(0x3002), None) == arg   # meta 4 B
+    assert L.hqq_dequantize_scales(q, m, 100, 128, C.c_void_p(0x4008), None) == arg
+    assert L.hqq_dequantize_scales(q, m, 100, 128, None, None) == arg
+    assert "scale_group" in L.hqq_last_error().decode() or L.hqq_last_error().decode() != ""

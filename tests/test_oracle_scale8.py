@@ -1,6 +1,6 @@
 """Pins of the oracle's 8-bit scales (CPU only).
 
-The pages quantize the per-group scales of the HQQ_g16_s variant to 8 bit in groups of 128
+The pages' HQQ_g16_s variant stores its per-group scales on 8-bit grids, one per 128 scales
 [techreport.ngo, "Half-Quadratic Quantization of Large Machine Learning Models", section
 "Benchmark results / Llama-2", note on the HQQ_g16_s row]. The reading (min-max affine uint8
 round-to-nearest per group of scales, like the 8-bit zero-point) is pinned here against
