@@ -222,6 +222,38 @@ class Oracle:
         r["packed"] = self.pack(r["codes"], nbits)
         return r
 
+    def quantize_axis0(self, w16, rows, cols, group_size, nbits, p=0.7, beta=1.0, kappa=1.01,
+                       iters=20, early_stop=1, zero_bits=16):
+        """Whole tensor with groups down the columns (axis 0) [SK "Quantization configuration",
+        axis]. Reading: group (b, j) is W[b*g:(b+1)*g, j]; the per-group solver is unchanged.
+        Per-group outputs (scale, zero, s, passes, ...) form a [rows/g, cols] row-major array,
+        group (b, j) at b*cols + j; the codes stay in the tensor's row-major order, so the
+        packed stream has the same layout as for axis 1. The 8-bit zero grid is per tensor
+        (order-independent)."""
+        assert rows % group_size == 0
+        w = np.ascontiguousarray(w16, np.uint16).reshape(rows, cols)
+        cg = np.ascontiguousarray(w.T)                     # column j's runs, one after another
+        r = self.solve_groups(cg.reshape(-1), group_size, nbits, p, beta, kappa, iters,
+                              early_stop)
+        nb = rows // group_size
+        out = {}
+        for k, v in r.items():                             # per group: [cols, nb] -> [nb, cols]
+            out[k] = np.ascontiguousarray(v.reshape(cols, nb).T).reshape(-1) if k != "codes" \
+                else np.ascontiguousarray(v.reshape(cols, rows).T).reshape(-1)
+        if zero_bits == 16:
+            out["zero"] = self.zero_to_half(out["zero_f32"])
+            out["zero_meta"] = None
+        else:
+            out["zero"], out["zero_meta"] = self.zero_requant(out["zero_f32"])
+        out["packed"] = self.pack(out["codes"], nbits)
+        return out
+
+    def dequantize_axis0(self, codes, scale, zero, zero_meta, rows, cols, g, zero_bits):
+        """Reconstruction for axis 0: W_r[i, j] from group (i//g, j)'s scale and zero."""
+        rep = lambda a: np.ascontiguousarray(
+            np.repeat(np.asarray(a).reshape(rows // g, cols), g, axis=0)).reshape(-1)
+        return self.dequantize(codes, rep(scale), rep(zero), zero_meta, 1, zero_bits)
+
     def packed_bytes(self, n, nbits) -> int:
         return int(self.L.hqo_packed_bytes(n, nbits))
 
