@@ -158,6 +158,49 @@ def scale8_row(dev, stream, reps=10):
     return row
 
 
+def axis0_row(specs, weights, dev, stream, axis1_solve_ms, reps=3):
+    """The same stack with groups down columns (axis 0): the solve phase transposes each
+    weight matrix (2 B read + 2 B written per weight) and runs the unchanged solver on the
+    transposed copy; the requant phase writes codes and per-group arrays back in the
+    tensor's order: packed codes transposed in one pass through LDS (nbits/4 B per weight;
+    3-bit words take unpack, byte transpose and pack instead)."""
+    import torch
+    from calibration_free_weight_amd import hqq
+    jobs, outs = [], []
+    for s, w in zip(specs, weights):
+        o = hqq.alloc_outputs(s.rows, s.cols, s.nbits, s.group_size, s.zero_bits, dev)
+        jobs.append(hqq.make_job(w, s.nbits, s.group_size, 0, 0.7, 1.0, 1.01, 20, 1,
+                                 s.zero_bits, o["packed"], o["scale"], o["zero"],
+                                 o["zero_meta"]))
+        outs.append(o)
+    ws = hqq.alloc_workspace(jobs, dev)
+    hqq.hqq_quantize_batch(jobs, ws, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for k in range(reps):
+        ev[k][0].record(stream)
+        hqq.hqq_solve_batch(jobs, ws, stream.cuda_stream)
+        ev[k][1].record(stream)
+        hqq.hqq_requant_batch(jobs, ws, stream.cuda_stream)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    solve = sum(e[0].elapsed_time(e[1]) for e in ev) / reps
+    req = sum(e[1].elapsed_time(e[2]) for e in ev) / reps
+    n = sum(s.numel for s in specs)
+    glue = (solve - axis1_solve_ms) + req
+    # W transpose 4 B; codes: one fused pass (nbits/4 B) where rows start on a byte, else
+    # unpack + byte transpose + pack (4 + nbits/4 B); per-group arrays left out
+    glue_bytes = sum(s.numel * (4 + s.nbits / 4 + (0 if s.nbits != 3 else 4)) for s in specs)
+    del jobs, outs, ws
+    return {"variant": "groups down columns (axis 0), same stack", "ms_per_stack": round(solve + req, 3),
+            "value_gbs": round(2.0 * n / ((solve + req) * 1e-3) / 1e9, 1),
+            "solve_phase_ms": round(solve, 3), "requant_phase_ms": round(req, 3),
+            "axis1_solve_ms": round(axis1_solve_ms, 3), "glue_ms": round(glue, 3),
+            "glue_bytes_per_weight": round(glue_bytes / n, 4), "bound": "hbm",
+            "glue_achieved_gbs": round(glue_bytes / (glue * 1e-3) / 1e9, 1) if glue > 0 else None,
+            "peak": HBM_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -298,6 +341,9 @@ def main():
     }
     log("bench: 8-bit scales")
     result["next_rows"] = {"scale8": scale8_row(dev, stream)}
+    if args.workload == 2:
+        log("bench: axis 0")
+        result["next_rows"]["axis0"] = axis0_row(specs, weights, dev, stream, solve_ms)
     if not args.no_cpu_baseline:
         log("bench: timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(specs, weights, args.cpu_seconds)

@@ -46,11 +46,12 @@ hqq_status check_layout(int64_t rows, int64_t cols, int nbits, int group_size, i
     if (rows > 0 && cols > (int64_t(1) << 40) / rows)
         return fail(HQQ_ERR_ARG, who + "rows*cols too large");
     if (!valid_bits(nbits)) return fail(HQQ_ERR_ARG, who + "nbits must be 1, 2, 3, 4 or 8");
-    if (axis == 0)
-        return fail(HQQ_ERR_UNSUPPORTED, who + "axis=0 (groups down columns) is not built");
-    if (axis != 1) return fail(HQQ_ERR_ARG, who + "axis must be 0 or 1");
+    if (axis != 0 && axis != 1) return fail(HQQ_ERR_ARG, who + "axis must be 0 or 1");
     if (group_size <= 0) return fail(HQQ_ERR_ARG, who + "group_size must be > 0");
-    if (cols % group_size != 0) return fail(HQQ_ERR_ARG, who + "group_size must divide cols");
+    if (axis == 1 && cols % group_size != 0)
+        return fail(HQQ_ERR_ARG, who + "group_size must divide cols (axis 1)");
+    if (axis == 0 && rows % group_size != 0)
+        return fail(HQQ_ERR_ARG, who + "group_size must divide rows (axis 0)");
     if (!built_group(group_size))
         return fail(HQQ_ERR_UNSUPPORTED, who + "group_size must be 16, 32, 64, 128 or 256");
     return HQQ_OK;
@@ -98,8 +99,21 @@ hqq_status device_fail(hipError_t e, const std::string &what)
 //   binary32 zero staging of every 8-bit-zero job (first, so a one-job call finds its zeros
 //   at offset 0), the 3-bit boundary stash of every 3-bit job, per-job (min, max) keys, the
 //   device job table and one tile counter per class; each section 256-byte aligned.
+// An axis-0 job runs the group solver on its transposed weights ([cols, rows], whose rows
+// hold the column runs); the solver's outputs, in that order, are written back in the
+// tensor's order after the solve.
+struct Axis0 {
+    const hqq_job *src;
+    uint16_t *wt;          // transposed weights; after the solve, 2n bytes of code staging
+    uint8_t *packed_t;     // packed codes of the transposed tensor
+    uint16_t *scale_t;     // [cols, rows/g]
+    void *zero_t;          // binary16 or uint8 [cols, rows/g]
+    uint8_t *passes_t;     // or nullptr
+};
+
 struct Plan {
     std::vector<hqq::DevJob> table;      // in class order
+    std::vector<Axis0> ax0;
     std::vector<int> first;              // first table index of each class
     std::vector<int64_t> tiles;          // tiles of each class
     std::vector<const hqq_job *> src;    // host job of each table entry
@@ -144,6 +158,16 @@ void make_plan(const hqq_job *jobs, int n_jobs, char *ws, Plan &P)
         s_off[t] = off;
         if (j.nbits == 3) off += round_up(sizeof(uint2) * (size_t)ng);
     }
+    std::vector<size_t> a_off(n);
+    for (int t = 0; t < n; ++t) {
+        const hqq_job &j = jobs[order[t]];
+        if (j.axis != 0) continue;
+        const int64_t nw = j.rows * j.cols, ng = nw / j.group_size;
+        a_off[t] = off;
+        off += round_up(2 * (size_t)nw) + round_up(packed_bytes(nw, j.nbits)) +
+               round_up(2 * (size_t)ng) + round_up((j.zero_bits == 16 ? 2 : 1) * (size_t)ng) +
+               (j.passes ? round_up((size_t)ng) : 0);
+    }
     const size_t off_mm = off;
     off += round_up(sizeof(uint32_t) * 2 * (size_t)(n > 0 ? n : 1));
     P.off_table = off;
@@ -168,14 +192,35 @@ void make_plan(const hqq_job *jobs, int n_jobs, char *ws, Plan &P)
             d.nbits = j.nbits;
             d.g = j.group_size;
             d.item0 = item;
+            if (ws && j.axis == 0) {
+                const int64_t nw = j.rows * j.cols;
+                Axis0 a{};
+                a.src = &j;
+                char *p = ws + a_off[t];
+                a.wt = reinterpret_cast<uint16_t *>(p);
+                p += round_up(2 * (size_t)nw);
+                a.packed_t = reinterpret_cast<uint8_t *>(p);
+                p += round_up(packed_bytes(nw, j.nbits));
+                a.scale_t = reinterpret_cast<uint16_t *>(p);
+                p += round_up(2 * (size_t)ng);
+                a.zero_t = p;
+                p += round_up((j.zero_bits == 16 ? 2 : 1) * (size_t)ng);
+                a.passes_t = j.passes ? reinterpret_cast<uint8_t *>(p) : nullptr;
+                d.W = a.wt;
+                d.packed = a.packed_t;
+                d.scale = a.scale_t;
+                d.passes = a.passes_t;
+                P.ax0.push_back(a);
+            }
             if (ws) {
+                const bool t0 = j.axis == 0;
                 if (j.zero_bits == 8) {
                     d.zero32 = reinterpret_cast<float *>(ws + z_off[t]);
                     d.minmax = reinterpret_cast<uint32_t *>(ws + off_mm) + 2 * t;
-                    d.zq = static_cast<uint8_t *>(j.zero);
+                    d.zq = static_cast<uint8_t *>(t0 ? P.ax0.back().zero_t : j.zero);
                     d.meta = static_cast<uint16_t *>(j.zero_meta);
                 } else {
-                    d.zero16 = static_cast<uint16_t *>(j.zero);
+                    d.zero16 = static_cast<uint16_t *>(t0 ? P.ax0.back().zero_t : j.zero);
                 }
                 if (j.nbits == 3) d.stash = reinterpret_cast<uint2 *>(ws + s_off[t]);
             }
@@ -234,6 +279,13 @@ hqq_status run_batch(const hqq_job *jobs, int n_jobs, void *workspace, size_t wo
     uint32_t *counters = reinterpret_cast<uint32_t *>(ws + P.off_counters);
     const int n_classes = (int)P.first.size() - 1;
     if (phases & kSolve) {
+        if (!P.ax0.empty()) {                    // the column runs become rows
+            std::vector<hqq::XTask> x;
+            for (const Axis0 &a : P.ax0)
+                x.push_back({a.src->W, a.wt, a.src->rows, a.src->cols, hqq::kX16, 0});
+            hipError_t e = hqq::launch_transposes(x.data(), (int)x.size(), s);
+            if (e != hipSuccess) return device_fail(e, "axis-0 transpose launch");
+        }
         for (int o = 0; o < n; o += hqq::kFillJobs) {
             hqq::FillArgs f{};
             f.n = n - o < hqq::kFillJobs ? n - o : hqq::kFillJobs;
@@ -263,6 +315,34 @@ hqq_status run_batch(const hqq_job *jobs, int n_jobs, void *workspace, size_t wo
     if (phases & kRequant) {
         hipError_t e = hqq::launch_finish(table, n, P.n_items, s);
         if (e != hipSuccess) return device_fail(e, "zero requantization launch");
+        // axis-0 outputs back in the tensor's order: packed codes in one pass where every
+        // row starts on a byte (else unpacked, transposed and packed), and the per-group
+        // [cols, rows/g] arrays; the transposes of all jobs share launches
+        std::vector<hqq::XTask> x;
+        for (const Axis0 &a : P.ax0) {
+            const hqq_job &j = *a.src;
+            const int64_t nw = j.rows * j.cols, nb = j.rows / j.group_size;
+            if (hqq::codes_transpose_fused(j.nbits, j.rows, j.cols)) {
+                x.push_back({a.packed_t, j.packed, j.rows, j.cols, hqq::kXCodes, j.nbits});
+            } else {                             // 3-bit words, or rows not byte-aligned
+                uint8_t *ct = reinterpret_cast<uint8_t *>(a.wt), *c = ct + nw;
+                e = hqq::launch_unpack(a.packed_t, nw, j.nbits, ct, s);
+                if (e == hipSuccess) {
+                    const hqq::XTask t{ct, c, j.cols, j.rows, hqq::kX8, 0};
+                    e = hqq::launch_transposes(&t, 1, s);
+                }
+                if (e == hipSuccess)
+                    e = hqq::launch_pack(c, nw, j.nbits, static_cast<uint8_t *>(j.packed), s);
+                if (e != hipSuccess) return device_fail(e, "axis-0 code write-back launch");
+            }
+            x.push_back({a.scale_t, j.scale, j.cols, nb, hqq::kX16, 0});
+            x.push_back({a.zero_t, j.zero, j.cols, nb, j.zero_bits == 16 ? hqq::kX16 : hqq::kX8, 0});
+            if (a.passes_t) x.push_back({a.passes_t, j.passes, j.cols, nb, hqq::kX8, 0});
+        }
+        if (!x.empty()) {
+            e = hqq::launch_transposes(x.data(), (int)x.size(), s);
+            if (e != hipSuccess) return device_fail(e, "axis-0 write-back launch");
+        }
     }
     g_last_error.clear();
     return HQQ_OK;
@@ -347,7 +427,8 @@ hqq_status hqq_dequantize(const void *packed, const void *scale, const void *zer
     hipError_t e = hqq::launch_dequant(static_cast<const uint8_t *>(packed),
                                        static_cast<const uint16_t *>(scale), zero,
                                        static_cast<const uint16_t *>(zero_meta), n, nbits,
-                                       group_size, zero_bits, static_cast<uint16_t *>(W_out),
+                                       group_size, zero_bits, cols, axis,
+                                       static_cast<uint16_t *>(W_out),
                                        static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(e, "dequantize launch");
     g_last_error.clear();

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "hqq_internal.h"
 
@@ -98,7 +99,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t *packed,
                                                       const uint16_t *scale, const void *zero,
                                                       const uint16_t *meta, int64_t n,
                                                       int nbits, int g, int zero_bits,
-                                                      uint16_t *out)
+                                                      int64_t cols, int axis, uint16_t *out)
 {
     const int per = nbits == 3 ? 10 : 16;
     const int64_t chunks = (n + per - 1) / per;
@@ -113,7 +114,8 @@ __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t *packed,
         for (int j = 0; j < per; ++j) {
             const int64_t k = k0 + j;
             if (k >= n) break;
-            const int64_t gi = k / g;
+            // axis 1: group k/g; axis 0: group (row/g, col) of a [rows/g, cols] array
+            const int64_t gi = axis == 1 ? k / g : (k / cols / g) * cols + k % cols;
             const float zf = zero_bits == 16
                                  ? h2f(reinterpret_cast<const uint16_t *>(zero)[gi])
                                  : fmaf((float)reinterpret_cast<const uint8_t *>(zero)[gi], m0, m1);
@@ -318,6 +320,153 @@ __global__ void __launch_bounds__(256) scale_dequant_kernel(const uint8_t *__res
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Transposes of row-major [R, C] arrays to [C, R] (axis-0 grouping runs the group solver on
+// the transposed weights and writes its outputs back in the tensor's order). One launch
+// serves a list of arrays (the tensors of a batch): its 64 x 64 tiles are numbered across
+// the list, and each block finds its array by binary search. Reads and writes are whole
+// 64-element tile rows.
+// ---------------------------------------------------------------------------------------
+enum XSub { kXGen16, kXWhole16, kXGen8, kXCodes1, kXCodes2, kXCodes4, kXCodes8, kXWide1,
+            kXWide2, kXWide4, kXWide8 };
+
+struct XTaskDev {
+    const void *src;
+    void *dst;
+    int64_t R, C, tile0;
+    int sub;
+};
+constexpr int kXTasks = 48;
+struct XArgs {
+    XTaskDev t[kXTasks];
+    int n;
+    int64_t tiles;
+};
+
+template <typename T>
+__device__ void xtile_generic(const T *__restrict__ src, int64_t R, int64_t C, T *__restrict__ dst,
+                              int64_t r0, int64_t c0, T (*tile)[65])
+{
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int64_t r = r0 + ty + 4 * k, c = c0 + tx;
+        if (r < R && c < C) tile[ty + 4 * k][tx] = src[r * C + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int64_t c = c0 + ty + 4 * k, r = r0 + tx;
+        if (r < R && c < C) dst[c * R + r] = tile[tx][ty + 4 * k];
+    }
+}
+
+// binary16, whole tiles (R and C multiples of 64): 8-byte loads and stores, 16 threads per
+// 128-byte tile row.
+__device__ void xtile_whole16(const uint16_t *__restrict__ src, int64_t R, int64_t C,
+                              uint16_t *__restrict__ dst, int64_t r0, int64_t c0,
+                              uint16_t (*tile)[68])
+{
+    const int q = threadIdx.x & 15, w = threadIdx.x >> 4;    // 4-element quad, row
+    v2u in[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        in[k] = *reinterpret_cast<const v2u *>(src + (r0 + w + 16 * k) * C + c0 + 4 * q);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint16_t *row = &tile[w + 16 * k][4 * q];
+        row[0] = (uint16_t)in[k].x;
+        row[1] = (uint16_t)(in[k].x >> 16);
+        row[2] = (uint16_t)in[k].y;
+        row[3] = (uint16_t)(in[k].y >> 16);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int c = w + 16 * k;                              // output row = input column
+        const v2u o = {(uint32_t)tile[4 * q][c] | (uint32_t)tile[4 * q + 1][c] << 16,
+                       (uint32_t)tile[4 * q + 2][c] | (uint32_t)tile[4 * q + 3][c] << 16};
+        *reinterpret_cast<v2u *>(dst + (c0 + c) * R + r0 + 4 * q) = o;
+    }
+}
+
+// Packed NB-bit codes of [C, R] (row-major stream) to the packed stream of [R, C], for NB in
+// {1, 2, 4, 8} when every row of both streams starts on a byte (R*NB, C*NB multiples of 8);
+// WIDE: on a 4-byte boundary (multiples of 32), moved as 32-bit words. Here R, C and the
+// tile origin (r0, c0) are those of the output.
+template <int NB, bool WIDE>
+__device__ void xtile_codes(const uint8_t *__restrict__ src, int64_t R, int64_t C,
+                            uint8_t *__restrict__ dst, int64_t r0, int64_t c0,
+                            uint8_t (*tile)[65])
+{
+    using W = typename std::conditional<WIDE, uint32_t, uint8_t>::type;
+    constexpr int PER = 8 * (int)sizeof(W) / NB;   // codes per word
+    constexpr int RB = 64 / PER;                // words per 64-code tile row
+    // source row c (output column c) holds output rows r0.. as RB words
+    for (int e = threadIdx.x; e < 64 * RB; e += 256) {
+        const int cc = e / RB, b = e % RB;
+        const int64_t c = c0 + cc, r = r0 + (int64_t)b * PER;
+        if (c < C && r < R) {
+            const uint32_t v = reinterpret_cast<const W *>(src)[(c * R + r) * NB / 8 / sizeof(W)];
+#pragma unroll
+            for (int u = 0; u < PER; ++u) tile[cc][b * PER + u] = (v >> (NB * u)) & ((1u << NB) - 1u);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 64 * RB; e += 256) {
+        const int rr = e / RB, b = e % RB;
+        const int64_t r = r0 + rr, c = c0 + (int64_t)b * PER;
+        if (r < R && c < C) {
+            uint32_t v = 0;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) v |= (uint32_t)tile[b * PER + u][rr] << (NB * u);
+            reinterpret_cast<W *>(dst)[(r * C + c) * NB / 8 / sizeof(W)] = (W)v;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256) xpose_kernel(XArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[64 * 68];
+    for (int64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+        int lo = 0, hi = a.n - 1;               // last task whose first tile <= tile
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.t[mid].tile0 <= tile) lo = mid;
+            else hi = mid - 1;
+        }
+        const XTaskDev T = a.t[lo];
+        // tiles cover the output for codes ([R, C]) and the input otherwise ([R, C] -> [C, R])
+        const int64_t lt = tile - T.tile0, tc = (T.C + 63) / 64;
+        const int64_t r0 = (lt / tc) * 64, c0 = (lt % tc) * 64;
+        const uint8_t *s8 = static_cast<const uint8_t *>(T.src);
+        uint8_t *d8 = static_cast<uint8_t *>(T.dst);
+        auto t8 = reinterpret_cast<uint8_t (*)[65]>(lds);
+        switch (T.sub) {
+        case kXGen16:
+            xtile_generic(static_cast<const uint16_t *>(T.src), T.R, T.C,
+                          static_cast<uint16_t *>(T.dst), r0, c0,
+                          reinterpret_cast<uint16_t (*)[65]>(lds));
+            break;
+        case kXWhole16:
+            xtile_whole16(static_cast<const uint16_t *>(T.src), T.R, T.C,
+                          static_cast<uint16_t *>(T.dst), r0, c0,
+                          reinterpret_cast<uint16_t (*)[68]>(lds));
+            break;
+        case kXGen8: xtile_generic(s8, T.R, T.C, d8, r0, c0, t8); break;
+        case kXCodes1: xtile_codes<1, false>(s8, T.R, T.C, d8, r0, c0, t8); break;
+        case kXCodes2: xtile_codes<2, false>(s8, T.R, T.C, d8, r0, c0, t8); break;
+        case kXCodes4: xtile_codes<4, false>(s8, T.R, T.C, d8, r0, c0, t8); break;
+        case kXCodes8: xtile_codes<8, false>(s8, T.R, T.C, d8, r0, c0, t8); break;
+        case kXWide1: xtile_codes<1, true>(s8, T.R, T.C, d8, r0, c0, t8); break;
+        case kXWide2: xtile_codes<2, true>(s8, T.R, T.C, d8, r0, c0, t8); break;
+        case kXWide4: xtile_codes<4, true>(s8, T.R, T.C, d8, r0, c0, t8); break;
+        default: xtile_codes<8, true>(s8, T.R, T.C, d8, r0, c0, t8); break;
+        }
+        __syncthreads();                        // the tile buffer is reused by the next tile
+    }
+}
+
 unsigned grid_for(int64_t items, int per_block)
 {
     int64_t b = (items + per_block - 1) / per_block;
@@ -339,12 +488,13 @@ hipError_t launch_finish(const DevJob *table, int n_jobs, int64_t n_items, hipSt
 
 hipError_t launch_dequant(const uint8_t *packed, const uint16_t *scale, const void *zero,
                           const uint16_t *meta, int64_t n, int nbits, int g, int zero_bits,
-                          uint16_t *out, hipStream_t stream)
+                          int64_t cols, int axis, uint16_t *out, hipStream_t stream)
 {
     if (n == 0) return hipSuccess;
     const int per = nbits == 3 ? 10 : 16;
     hipLaunchKernelGGL(dequant_kernel, dim3(grid_for((n + per - 1) / per, 256)), dim3(256), 0,
-                       stream, packed, scale, zero, meta, n, nbits, g, zero_bits, out);
+                       stream, packed, scale, zero, meta, n, nbits, g, zero_bits, cols, axis,
+                       out);
     return hipGetLastError();
 }
 
@@ -394,6 +544,46 @@ hipError_t launch_scale_dequant(const uint8_t *sq, const uint16_t *meta, int64_t
     hipLaunchKernelGGL(scale_dequant_kernel, dim3(grid_for((n + 7) / 8 / kScaleUnroll, 256)), dim3(256), 0,
                        stream, sq, meta, n, lg, out);
     return hipGetLastError();
+}
+
+bool codes_transpose_fused(int nbits, int64_t R, int64_t C)
+{
+    return nbits != 3 && (R * nbits) % 8 == 0 && (C * nbits) % 8 == 0;
+}
+
+hipError_t launch_transposes(const XTask *tasks, int n, hipStream_t stream)
+{
+    auto al = [](const void *p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; };
+    for (int o = 0; o < n; o += kXTasks) {
+        XArgs a{};
+        int64_t tiles = 0;
+        for (int i = o; i < n && i < o + kXTasks; ++i) {
+            const XTask &t = tasks[i];
+            if (t.R == 0 || t.C == 0) continue;
+            XTaskDev d{t.src, t.dst, t.R, t.C, tiles, 0};
+            if (t.kind == kX16) {
+                const bool whole = t.R % 64 == 0 && t.C % 64 == 0 && al(t.src, 8) && al(t.dst, 8);
+                d.sub = whole ? kXWhole16 : kXGen16;
+            } else if (t.kind == kX8) {
+                d.sub = kXGen8;
+            } else {
+                if (!codes_transpose_fused(t.nbits, t.R, t.C)) return hipErrorInvalidValue;
+                const bool wide = (t.R * t.nbits) % 32 == 0 && (t.C * t.nbits) % 32 == 0 &&
+                                  al(t.src, 4) && al(t.dst, 4);
+                const int lg = t.nbits == 1 ? 0 : t.nbits == 2 ? 1 : t.nbits == 4 ? 2 : 3;
+                d.sub = (wide ? kXWide1 : kXCodes1) + lg;
+            }
+            tiles += ((t.R + 63) / 64) * ((t.C + 63) / 64);
+            a.t[a.n++] = d;
+        }
+        a.tiles = tiles;
+        if (a.n == 0) continue;
+        const unsigned grid = (unsigned)(tiles < 65536 ? tiles : 65536);
+        hipLaunchKernelGGL(xpose_kernel, dim3(grid), dim3(256), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace hqq

@@ -55,7 +55,22 @@ hipError_t launch_finish(const DevJob *table, int n_jobs, int64_t n_items, hipSt
 
 hipError_t launch_dequant(const uint8_t *packed, const uint16_t *scale, const void *zero,
                           const uint16_t *meta, int64_t n, int nbits, int g, int zero_bits,
-                          uint16_t *out, hipStream_t stream);
+                          int64_t cols, int axis, uint16_t *out, hipStream_t stream);
+
+// Transposes of row-major arrays, many per launch. kX16 / kX8: [R, C] -> [C, R] of 2- or
+// 1-byte elements. kXCodes: the packed nbits-bit code stream of a [C, R] array -> that of
+// [R, C] (R, C of the output), only when codes_transpose_fused(nbits, R, C): 8/4/2/1 bits
+// with every row starting on a byte.
+enum XKind { kX16, kX8, kXCodes };
+struct XTask {
+    const void *src;
+    void *dst;
+    int64_t R, C;
+    XKind kind;
+    int nbits;
+};
+bool codes_transpose_fused(int nbits, int64_t R, int64_t C);
+hipError_t launch_transposes(const XTask *tasks, int n, hipStream_t stream);
 
 // 8-bit scales: scale_group a power of two in [8, 512]; buffers 16-byte aligned (meta 4).
 hipError_t launch_scale_requant(const uint16_t *scale, int64_t n, int scale_group, uint8_t *sq,

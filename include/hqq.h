@@ -26,7 +26,11 @@
  *  - Calls are reentrant; concurrent calls need distinct workspaces and outputs.
  *  - Layouts: W is binary16, row-major [rows, cols], contiguous. With axis = 1 a group is
  *    `group_size` consecutive elements of a row, so the tensor is a flat array of
- *    n_groups = rows*cols/group_size contiguous groups, numbered in memory order.
+ *    n_groups = rows*cols/group_size contiguous groups, numbered in memory order. With
+ *    axis = 0 a group is `group_size` consecutive elements of a column: group (b, j) is
+ *    W[b*g .. b*g+g-1][j], and per-group outputs (scale, zero, passes) form a row-major
+ *    [rows/g, cols] array (group (b, j) at b*cols + j). Either way the codes keep W's
+ *    row-major order.
  *  - Packed codes: one flat stream in memory order; code k of a container occupies bits
  *    [nbits*k, nbits*k + nbits). 8/4/2/1-bit codes fill uint8 containers (1/2/4/8 per byte);
  *    3-bit codes fill little-endian uint32 containers, 10 per word, bits 30-31 zero.
@@ -48,7 +52,7 @@ extern "C" {
 typedef enum hqq_status {
     HQQ_OK = 0,
     HQQ_ERR_ARG = 1,         /* invalid argument (null, misaligned, out of range)       */
-    HQQ_ERR_UNSUPPORTED = 2, /* valid for the method but not built here (e.g. axis = 0)  */
+    HQQ_ERR_UNSUPPORTED = 2, /* valid for the method but not built (e.g. group_size 8)    */
     HQQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than hqq_workspace_bytes()  */
     HQQ_ERR_DEVICE = 4       /* a HIP call failed; see hqq_last_error()                  */
 } hqq_status;
@@ -59,8 +63,8 @@ typedef struct hqq_job {
     const void *W;           /* binary16 [rows, cols], 16-byte aligned                     */
     int64_t rows, cols;
     int nbits;               /* 1, 2, 3, 4 or 8 [SK "Quantization configuration"]          */
-    int group_size;          /* 16, 32, 64, 128 or 256; divides cols                       */
-    int axis;                /* 1 (groups along rows); 0 -> HQQ_ERR_UNSUPPORTED            */
+    int group_size;          /* 16, 32, 64, 128 or 256; divides cols (axis 1) or rows (0)  */
+    int axis;                /* 1: groups along rows; 0: down columns (see Layouts)        */
     float p, beta, kappa;    /* lp exponent (0 < p <= 1), initial beta, beta growth [TR]   */
     int iters;               /* 0..254 half-quadratic iterations; 0 = min-max RTN          */
     int early_stop;          /* 1: stop a group when its error rises; 0: run all iters     */
@@ -78,8 +82,9 @@ size_t hqq_packed_bytes(int64_t n_codes, int nbits);
 
 /* Workspace bytes hqq_quantize_batch needs for these jobs (host array): the device copy of
  * the job table and its work counters, binary32 zero staging and per-tensor (min, max) for
- * 8-bit zero requantization, and the words that 3-bit groups share (0 if every tensor is
- * empty). Returns SIZE_MAX if a job is invalid; the quantize call then reports why. */
+ * 8-bit zero requantization, the words that 3-bit groups share, and for each axis-0 job a
+ * transposed copy of its weights and outputs (about 2 + nbits/8 bytes per weight); 0 if
+ * every tensor is empty. Returns SIZE_MAX if a job is invalid; the quantize call then reports why. */
 size_t hqq_workspace_bytes(const hqq_job *jobs, int n_jobs);
 
 /* Quantize one tensor [TR "Outlier-aware optimization without gradients"].
@@ -93,7 +98,7 @@ size_t hqq_workspace_bytes(const hqq_job *jobs, int n_jobs);
  * workspace: device buffer (256-byte aligned) of at least hqq_workspace_bytes() for this one
  * job (it holds the device job table; NULL only for an empty tensor). With zero_bits == 8
  * its first 4*n_groups bytes hold, after the call, the binary32 zeros the solver returned
- * (before 8-bit requantization). */
+ * (before 8-bit requantization; for axis 0 in column-major group order, j*(rows/g) + b). */
 hqq_status hqq_quantize(const void *W, int64_t rows, int64_t cols, int nbits, int group_size,
                         int axis, float p, float beta, float kappa, int iters, int early_stop,
                         int zero_bits, void *packed, void *scale, void *zero, void *zero_meta,
@@ -110,8 +115,9 @@ hqq_status hqq_quantize_batch(const hqq_job *jobs, int n_jobs, void *workspace,
  * passes and, for zero_bits == 16, the binary16 zeros; for zero_bits == 8 it leaves the
  * binary32 zeros and their per-tensor reduction inputs in the workspace.
  * hqq_requant_batch then quantizes those zeros to 8 bit [TR "Benchmark results / Llama-2"]
- * and writes zero and zero_meta. It must be given the same jobs and workspace, after
- * hqq_solve_batch on the same stream (it does nothing for zero_bits == 16 jobs). */
+ * and writes zero and zero_meta, joins the 3-bit words two groups share, and writes every
+ * output of axis-0 jobs (solved in transposed order) back in the tensor's order. It must be
+ * given the same jobs and workspace, after hqq_solve_batch on the same stream. */
 hqq_status hqq_solve_batch(const hqq_job *jobs, int n_jobs, void *workspace,
                            size_t workspace_bytes, void *stream);
 hqq_status hqq_requant_batch(const hqq_job *jobs, int n_jobs, void *workspace,
@@ -119,7 +125,8 @@ hqq_status hqq_requant_batch(const hqq_job *jobs, int n_jobs, void *workspace,
 
 /* Reconstruct binary16 weights [SK "HQQLinear layer", dequantize()]:
  * W_out = binary16((q - zero_f) * scale), zero_f the binary16 zero or, for zero_bits == 8,
- * zq * zero_meta[0] + zero_meta[1] (one fused rounding). Same layouts as hqq_quantize. */
+ * zq * zero_meta[0] + zero_meta[1] (one fused rounding), with each element's group found
+ * by `axis`. Same layouts as hqq_quantize. */
 hqq_status hqq_dequantize(const void *packed, const void *scale, const void *zero,
                           const void *zero_meta, int64_t rows, int64_t cols, int nbits,
                           int group_size, int axis, int zero_bits, void *W_out, void *stream);

@@ -50,7 +50,7 @@ def _job(H, **kw):
 
 
 BAD = [
-    (dict(nbits=5), 1), (dict(nbits=0), 1), (dict(axis=0), 2), (dict(axis=2), 1),
+    (dict(nbits=5), 1), (dict(nbits=0), 1), (dict(axis=0, rows=72), 1), (dict(axis=2), 1),
     (dict(group_size=48), 1), (dict(group_size=0), 1), (dict(group_size=8, cols=256), 2),
     (dict(p=0.0), 1), (dict(p=1.5), 1), (dict(p=float("nan")), 1), (dict(beta=0.0), 1),
     (dict(kappa=-1.0), 1), (dict(iters=-1), 1), (dict(iters=255), 1), (dict(early_stop=2), 1),
@@ -104,7 +104,14 @@ def test_other_entry_points_validate(H):
     assert L.hqq_unpack(C.c_void_p(0x1001), 10, 3, C.c_void_p(0x2000), None) == H.HQQ_ERR_ARG
     assert L.hqq_dequantize(C.c_void_p(0x1000), C.c_void_p(0x2000), C.c_void_p(0x3000), None,
                             4, 64, 4, 64, 1, 8, C.c_void_p(0x4000), None) == H.HQQ_ERR_ARG
+    # axis 0 needs group_size to divide rows; then the null buffers are the error
     assert L.hqq_dequantize(None, None, None, None, 4, 64, 4, 64, 0, 16, None, None) == \
+        H.HQQ_ERR_ARG
+    assert "divide rows" in L.hqq_last_error().decode()
+    assert L.hqq_dequantize(None, None, None, None, 128, 3, 4, 64, 0, 16, None, None) == \
+        H.HQQ_ERR_ARG
+    assert "non-null" in L.hqq_last_error().decode()
+    assert L.hqq_dequantize(None, None, None, None, 128, 3, 4, 8, 0, 16, None, None) == \
         H.HQQ_ERR_UNSUPPORTED
 
 
