@@ -348,6 +348,45 @@ hqq_status run_batch(const hqq_job *jobs, int n_jobs, void *workspace, size_t wo
     return HQQ_OK;
 }
 
+// ---- host-streamed batches ----------------------------------------------------------------
+// Consecutive jobs are cut into chunks whose weights fit half of the staging buffer (each
+// tensor at a 256-byte aligned offset); chunk k is copied into half k % 2.
+struct Chunk {
+    int first, count;
+};
+
+hqq_status make_chunks(const hqq_job *jobs, int n_jobs, size_t staging_bytes,
+                       std::vector<Chunk> &out)
+{
+    const size_t half = staging_bytes / 2 / kAlign * kAlign;
+    size_t used = 0;
+    int first = 0;
+    for (int i = 0; i < n_jobs; ++i) {
+        const size_t b = round_up(2 * (size_t)(jobs[i].rows * jobs[i].cols));
+        if (b > half)
+            return fail(HQQ_ERR_WORKSPACE, job_name(i) + "its weights (" + std::to_string(b) +
+                                               " bytes) exceed half the staging buffer");
+        if (used + b > half) {
+            out.push_back({first, i - first});
+            first = i;
+            used = 0;
+        }
+        used += b;
+    }
+    if (n_jobs > first) out.push_back({first, n_jobs - first});
+    return HQQ_OK;
+}
+
+size_t streamed_workspace(const hqq_job *jobs, const std::vector<Chunk> &chunks)
+{
+    size_t need = 0;
+    for (const Chunk &c : chunks) {
+        const size_t b = batch_workspace(jobs + c.first, c.count);
+        need = b > need ? b : need;
+    }
+    return need;
+}
+
 }  // namespace
 
 extern "C" {
@@ -379,6 +418,94 @@ hqq_status hqq_requant_batch(const hqq_job *jobs, int n_jobs, void *workspace,
                              size_t workspace_bytes, void *stream)
 {
     return run_batch(jobs, n_jobs, workspace, workspace_bytes, stream, kRequant);
+}
+
+size_t hqq_streamed_workspace_bytes(const hqq_job *jobs, int n_jobs, size_t staging_bytes)
+{
+    if (n_jobs < 0 || (n_jobs > 0 && !jobs) || n_jobs > 65535) return SIZE_MAX;
+    for (int i = 0; i < n_jobs; ++i)
+        if (check_job(jobs[i], i) != HQQ_OK) return SIZE_MAX;
+    std::vector<Chunk> chunks;
+    if (make_chunks(jobs, n_jobs, staging_bytes, chunks) != HQQ_OK) return SIZE_MAX;
+    return streamed_workspace(jobs, chunks);
+}
+
+hqq_status hqq_quantize_streamed(const hqq_job *jobs, int n_jobs, void *staging,
+                                 size_t staging_bytes, void *workspace, size_t workspace_bytes,
+                                 void *stream, void *copy_stream)
+{
+    if (n_jobs < 0) return fail(HQQ_ERR_ARG, "n_jobs must be >= 0");
+    if (n_jobs > 0 && !jobs) return fail(HQQ_ERR_ARG, "jobs must be non-null");
+    if (n_jobs > 65535) return fail(HQQ_ERR_ARG, "at most 65535 jobs per batch");
+    for (int i = 0; i < n_jobs; ++i) {
+        hqq_status st = check_job(jobs[i], n_jobs > 1 ? i : -1);
+        if (st != HQQ_OK) return st;
+    }
+    std::vector<Chunk> chunks;
+    hqq_status st = make_chunks(jobs, n_jobs, staging_bytes, chunks);
+    if (st != HQQ_OK) return st;
+    bool any = false;
+    for (int i = 0; i < n_jobs; ++i) any = any || jobs[i].rows * jobs[i].cols > 0;
+    if (!any) {
+        g_last_error.clear();
+        return HQQ_OK;
+    }
+    if (!staging || !aligned(staging, kAlign))
+        return fail(HQQ_ERR_ARG, "staging must be non-null and 256-byte aligned");
+    const size_t need = streamed_workspace(jobs, chunks);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(HQQ_ERR_WORKSPACE, "workspace must hold " + std::to_string(need) + " bytes");
+    if (need > 0 && !aligned(workspace, kAlign))
+        return fail(HQQ_ERR_ARG, "workspace must be 256-byte aligned");
+
+    hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(copy_stream);
+    // copied[h]: half h holds its chunk; consumed[h]: the solve of half h's chunk is done
+    hipEvent_t copied[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr};
+    hipError_t e = hipSuccess;
+    for (int h = 0; h < 2 && e == hipSuccess; ++h) {
+        e = hipEventCreateWithFlags(&copied[h], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&consumed[h], hipEventDisableTiming);
+    }
+    auto release = [&]() {                       // safe while recorded work is pending
+        for (int h = 0; h < 2; ++h) {
+            if (copied[h]) (void)hipEventDestroy(copied[h]);
+            if (consumed[h]) (void)hipEventDestroy(consumed[h]);
+        }
+    };
+    if (e != hipSuccess) {
+        release();
+        return device_fail(e, "event creation");
+    }
+    const size_t half = staging_bytes / 2 / kAlign * kAlign;
+    std::vector<hqq_job> local;
+    for (size_t k = 0; k < chunks.size() && st == HQQ_OK; ++k) {
+        const Chunk &c = chunks[k];
+        const int h = (int)(k % 2);
+        char *dst = static_cast<char *>(staging) + h * half;
+        if (k >= 2) e = hipStreamWaitEvent(cs, consumed[h], 0);   // chunk k-2 left this half
+        local.assign(jobs + c.first, jobs + c.first + c.count);
+        size_t off = 0;
+        for (int i = 0; i < c.count && e == hipSuccess; ++i) {
+            const size_t b = 2 * (size_t)(local[i].rows * local[i].cols);
+            if (b > 0) e = hipMemcpyAsync(dst + off, local[i].W, b, hipMemcpyHostToDevice, cs);
+            local[i].W = dst + off;
+            off += round_up(b);
+        }
+        if (e == hipSuccess) e = hipEventRecord(copied[h], cs);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, copied[h], 0);
+        if (e != hipSuccess) {
+            st = device_fail(e, "weight upload");
+            break;
+        }
+        st = run_batch(local.data(), c.count, workspace, workspace_bytes, stream, kSolve | kRequant);
+        if (st == HQQ_OK) {
+            e = hipEventRecord(consumed[h], s);
+            if (e != hipSuccess) st = device_fail(e, "event record");
+        }
+    }
+    release();
+    if (st == HQQ_OK) g_last_error.clear();
+    return st;
 }
 
 hqq_status hqq_quantize(const void *W, int64_t rows, int64_t cols, int nbits, int group_size,

@@ -17,7 +17,8 @@ HQQ_OK, HQQ_ERR_ARG, HQQ_ERR_UNSUPPORTED, HQQ_ERR_WORKSPACE, HQQ_ERR_DEVICE = ra
 
 # Functions declared in include/hqq.h (checked by the tests against the header).
 EXPORTS = ("hqq_packed_bytes", "hqq_workspace_bytes", "hqq_quantize", "hqq_quantize_batch",
-           "hqq_solve_batch", "hqq_requant_batch", "hqq_dequantize", "hqq_requant_scales",
+           "hqq_solve_batch", "hqq_requant_batch", "hqq_quantize_streamed",
+           "hqq_streamed_workspace_bytes", "hqq_dequantize", "hqq_requant_scales",
            "hqq_dequantize_scales", "hqq_pack", "hqq_unpack", "hqq_status_string",
            "hqq_last_error")
 
@@ -58,6 +59,11 @@ def lib():
         for name in ("hqq_quantize_batch", "hqq_solve_batch", "hqq_requant_batch"):
             getattr(L, name).restype = i32
             getattr(L, name).argtypes = [C.POINTER(hqq_job), i32, vp, C.c_size_t, vp]
+        L.hqq_quantize_streamed.restype = i32
+        L.hqq_quantize_streamed.argtypes = [C.POINTER(hqq_job), i32, vp, C.c_size_t, vp,
+                                            C.c_size_t, vp, vp]
+        L.hqq_streamed_workspace_bytes.restype = C.c_size_t
+        L.hqq_streamed_workspace_bytes.argtypes = [C.POINTER(hqq_job), i32, C.c_size_t]
         L.hqq_dequantize.restype = i32
         L.hqq_dequantize.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp]
         L.hqq_requant_scales.restype = i32
@@ -148,6 +154,24 @@ def hqq_solve_batch(jobs, workspace, stream=None) -> None:
 
 def hqq_requant_batch(jobs, workspace, stream=None) -> None:
     _batch(lib().hqq_requant_batch, jobs, workspace, stream)
+
+
+def hqq_streamed_workspace_bytes(jobs, staging_bytes) -> int:
+    arr = (hqq_job * len(jobs))(*jobs)
+    n = int(lib().hqq_streamed_workspace_bytes(arr, len(jobs), staging_bytes))
+    if n == (1 << 64) - 1:
+        raise HQQError(HQQ_ERR_ARG, "invalid job, or a tensor larger than half the staging")
+    return n
+
+
+def hqq_quantize_streamed(jobs, staging, workspace, stream=None, copy_stream=None) -> None:
+    """jobs[i].W are host pointers (pinned); staging and workspace are device tensors."""
+    arr = (hqq_job * len(jobs))(*jobs)
+    sb = staging.numel() * staging.element_size()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    cs = _stream(copy_stream) if copy_stream is not None else _stream(stream)
+    _check(lib().hqq_quantize_streamed(arr, len(jobs), _p(staging), sb, _p(workspace), wsb,
+                                       _stream(stream), cs))
 
 
 def hqq_dequantize(packed, scale, zero, zero_meta, rows, cols, nbits, group_size, axis,

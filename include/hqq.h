@@ -123,6 +123,27 @@ hqq_status hqq_solve_batch(const hqq_job *jobs, int n_jobs, void *workspace,
 hqq_status hqq_requant_batch(const hqq_job *jobs, int n_jobs, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* Quantize a batch whose weights live in HOST memory, for stacks larger than the device
+ * memory [SK "Common issues": when quantization runs out of memory, load the layers one after
+ * another; TR "Speed: from hours to minutes": each weight crosses to the GPU once]. jobs[i].W is a host pointer (allocate it pinned, e.g. with
+ * hipHostMalloc, for the copy to overlap the solve; pageable memory works but serialises);
+ * every output pointer is a device pointer, as for hqq_quantize_batch, with the same results.
+ * Consecutive jobs are cut into chunks whose weights fit half of `staging` (a device buffer,
+ * 256-byte aligned; each tensor takes 2*rows*cols bytes rounded up to 256): chunk k is
+ * copied into half k % 2 on `copy_stream` while chunk k-1 is solved on `stream`.
+ * `workspace` must hold hqq_streamed_workspace_bytes(jobs, n_jobs, staging_bytes). The
+ * call enqueues only (it creates four HIP events and releases them before returning); the
+ * host weights must stay valid and unchanged until `stream` has completed the work. A
+ * tensor larger than half the staging buffer -> HQQ_ERR_WORKSPACE. copy_stream may equal
+ * stream (no overlap). */
+hqq_status hqq_quantize_streamed(const hqq_job *jobs, int n_jobs, void *staging,
+                                 size_t staging_bytes, void *workspace, size_t workspace_bytes,
+                                 void *stream, void *copy_stream);
+
+/* Workspace bytes hqq_quantize_streamed needs with a staging buffer of staging_bytes (the
+ * largest chunk's batch workspace); SIZE_MAX if a job is invalid or does not fit. */
+size_t hqq_streamed_workspace_bytes(const hqq_job *jobs, int n_jobs, size_t staging_bytes);
+
 /* Reconstruct binary16 weights [SK "HQQLinear layer", dequantize()]:
  * W_out = binary16((q - zero_f) * scale), zero_f the binary16 zero or, for zero_bits == 8,
  * zq * zero_meta[0] + zero_meta[1] (one fused rounding), with each element's group found

@@ -133,3 +133,26 @@ def test_scale_entry_points_validate(H):
     assert L.hqq_dequantize_scales(q, m, 100, 128, C.c_void_p(0x4008), None) == arg
     assert L.hqq_dequantize_scales(q, m, 100, 128, None, None) == arg
     assert "scale_group" in L.hqq_last_error().decode() or L.hqq_last_error().decode() != ""
+
+
+def test_streamed_entry_points_validate(H):
+    L = H.lib()
+    j = _job(H, rows=64, cols=256)                       # 32 KiB of binary16 weights
+    arr = (H.hqq_job * 2)(j, _job(H, rows=128, cols=256, W=0x9000))
+    big = 1 << 20
+    assert L.hqq_streamed_workspace_bytes(arr, 2, big) not in (0, 2 ** 64 - 1)
+    assert L.hqq_streamed_workspace_bytes(arr, 2, 2 * 32768) == 2 ** 64 - 1   # 64 KiB tensor
+    st = L.hqq_quantize_streamed(arr, 2, C.c_void_p(0x100000), 2 * 32768, None, 0, None, None)
+    assert st == H.HQQ_ERR_WORKSPACE and "half the staging" in L.hqq_last_error().decode()
+    st = L.hqq_quantize_streamed(arr, 2, None, big, C.c_void_p(0x200000), big, None, None)
+    assert st == H.HQQ_ERR_ARG and "staging" in L.hqq_last_error().decode()
+    st = L.hqq_quantize_streamed(arr, 2, C.c_void_p(0x100010), big, C.c_void_p(0x200000), big,
+                                 None, None)
+    assert st == H.HQQ_ERR_ARG                            # staging not 256-byte aligned
+    st = L.hqq_quantize_streamed(arr, 2, C.c_void_p(0x100000), big, None, 0, None, None)
+    assert st == H.HQQ_ERR_WORKSPACE
+    bad = (H.hqq_job * 1)(_job(H, nbits=5))
+    assert L.hqq_quantize_streamed(bad, 1, C.c_void_p(0x100000), big, None, 0, None, None) == \
+        H.HQQ_ERR_ARG
+    empty = (H.hqq_job * 1)(_job(H, rows=0))
+    assert L.hqq_quantize_streamed(empty, 1, None, 0, None, 0, None, None) == H.HQQ_OK
