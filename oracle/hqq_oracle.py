@@ -254,6 +254,16 @@ class Oracle:
             np.repeat(np.asarray(a).reshape(rows // g, cols), g, axis=0)).reshape(-1)
         return self.dequantize(codes, rep(scale), rep(zero), zero_meta, 1, zero_bits)
 
+    def gemm(self, x16, codes, scale, zero, zero_meta, n, k, g, zero_bits):
+        """The linear layer of a quantized weight [SK "HQQLinear layer": the layer computes with
+        the dequantized weight]: Y = X · W_r^T, W_r the binary16 reconstruction of the axis-1
+        quantized [n, k] weight (this oracle's dequantize), X binary16 [m, k]. Products of
+        binary16 values are exact in binary64; the sums are binary64 (numpy matmul)."""
+        w = self.dequantize(codes, scale, zero, zero_meta, g, zero_bits)
+        w = w.view(np.float16).astype(np.float64).reshape(n, k)
+        x = np.ascontiguousarray(x16, np.uint16).view(np.float16).astype(np.float64)
+        return x.reshape(-1, k) @ w.T
+
     def packed_bytes(self, n, nbits) -> int:
         return int(self.L.hqo_packed_bytes(n, nbits))
 
