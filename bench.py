@@ -260,6 +260,69 @@ def host_stream_row(specs, weights, dev, stream, reps=3):
             "overlap": round(copy_ms / ms, 4)}
 
 
+def gemm_row(specs, outs, dev, stream, reps=5):
+    """The quantized linear layers of the stack (hqq_gemm on the 224 quantized weights the
+    benchmark just wrote). Decode, M = 1: HBM-bound on the packed weights; the 224 calls are
+    captured in a HIP graph (launch gaps would dominate otherwise) and the replay is checked
+    against the eager result. Prefill, M = 512: the matrix-core path, 2*M*N*K flops."""
+    import torch
+    from calibration_free_weight_amd import hqq
+    kmax = max(s.cols for s in specs)
+    res = {"variant": "quantized linear layers of the stack, Y = X . W_r^T"}
+    for m in (1, 512):
+        X = torch.randn(m, kmax, device=dev).to(torch.float16)
+        Ys = [torch.empty(m, s.rows, dtype=torch.float16, device=dev) for s in specs]
+
+        Xs = {c: X[:, :c].contiguous() for c in {s.cols for s in specs}}
+
+        def run_all():
+            for s, o, Y in zip(specs, outs, Ys):
+                hqq.hqq_gemm(Xs[s.cols], o["packed"], o["scale"], o["zero"], o["zero_meta"],
+                             s.rows, s.cols, s.nbits, s.group_size, s.zero_bits, Y)
+        run_all()
+        torch.cuda.synchronize()
+        eager = [y.clone() for y in Ys]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        graphed = False
+        if m == 1:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_all()
+            for _ in range(2):
+                g.replay()
+                torch.cuda.synchronize()
+                assert all(torch.equal(a, b) for a, b in zip(eager, Ys)), "graph replay differs"
+            graphed = True
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        else:
+            e0.record(stream)
+            for _ in range(reps):
+                run_all()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        wbytes = sum(o["packed"].numel() + o["scale"].numel() * 2 +
+                     o["zero"].numel() * o["zero"].element_size() for o in outs)
+        nbytes = wbytes + sum(m * s.cols * 2 + m * s.rows * 2 for s in specs)
+        flops = sum(2.0 * m * s.rows * s.cols for s in specs)
+        row = {"m": m, "ms_per_stack": round(ms, 4), "graph": graphed,
+               "bytes": nbytes, "flops": flops,
+               "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+               "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+        if m == 1:
+            row.update(bound="hbm", achieved=row["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                       frac=round(row["hbm_gbs"] / HBM_PEAK_GBS, 4))
+        else:
+            row.update(bound="mfma", achieved=row["tflops"], peak=2500.0, unit="TFLOP/s",
+                       frac=round(row["tflops"] / 2500.0, 4))
+        res[f"m{m}"] = row
+        del X, Ys, eager, Xs
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -403,6 +466,8 @@ def main():
     if args.workload == 2:
         log("bench: axis 0")
         result["next_rows"]["axis0"] = axis0_row(specs, weights, dev, stream, solve_ms)
+        log("bench: quantized linear layers")
+        result["next_rows"]["gemm"] = gemm_row(specs, outs, dev, stream)
         log("bench: host streaming")
         result["next_rows"]["host_stream"] = host_stream_row(specs, weights, dev, stream)
     if not args.no_cpu_baseline:

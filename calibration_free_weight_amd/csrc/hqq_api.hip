@@ -607,6 +607,36 @@ hqq_status hqq_dequantize_scales(const uint8_t *scale_q, const void *scale_meta,
     return HQQ_OK;
 }
 
+hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *scale,
+                    const void *zero, const void *zero_meta, int64_t N, int64_t K, int nbits,
+                    int group_size, int zero_bits, void *Y, void *stream)
+{
+    hqq_status st = check_layout(N, K, nbits, group_size, 1, "");
+    if (st != HQQ_OK) return st;
+    if (M < 0) return fail(HQQ_ERR_ARG, "M must be >= 0");
+    if (M > 0 && K > (int64_t(1) << 40) / M) return fail(HQQ_ERR_ARG, "M*K too large");
+    if (zero_bits != 8 && zero_bits != 16) return fail(HQQ_ERR_ARG, "zero_bits must be 8 or 16");
+    if (M == 0 || N == 0) return HQQ_OK;
+    if (!X || !Y || (K > 0 && (!packed || !scale || !zero)))
+        return fail(HQQ_ERR_ARG, "X, Y, packed, scale and zero must be non-null");
+    if (zero_bits == 8 && K > 0 && !zero_meta)
+        return fail(HQQ_ERR_ARG, "zero_meta must be non-null when zero_bits == 8");
+    if (!aligned(X, 16)) return fail(HQQ_ERR_ARG, "X must be 16-byte aligned");
+    if (!aligned(Y, 2) || !aligned(scale, 2) || (zero_bits == 16 && !aligned(zero, 2)) ||
+        (zero_bits == 8 && !aligned(zero_meta, 2)))
+        return fail(HQQ_ERR_ARG, "binary16 buffers must be 2-byte aligned");
+    if (nbits == 3 && !aligned(packed, 4)) return fail(HQQ_ERR_ARG, "packed must be 4-byte aligned");
+    hipError_t e = hqq::launch_gemm(static_cast<const uint16_t *>(X), M,
+                                    static_cast<const uint8_t *>(packed),
+                                    static_cast<const uint16_t *>(scale), zero,
+                                    static_cast<const uint16_t *>(zero_meta), N, K, nbits,
+                                    group_size, zero_bits, static_cast<uint16_t *>(Y),
+                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "gemm launch");
+    g_last_error.clear();
+    return HQQ_OK;
+}
+
 hqq_status hqq_pack(const uint8_t *codes, int64_t n_codes, int nbits, void *packed, void *stream)
 {
     if (!valid_bits(nbits)) return fail(HQQ_ERR_ARG, "nbits must be 1, 2, 3, 4 or 8");

@@ -172,6 +172,17 @@ hqq_status hqq_requant_scales(const void *scale, int64_t n, int scale_group, uin
 hqq_status hqq_dequantize_scales(const uint8_t *scale_q, const void *scale_meta, int64_t n,
                                  int scale_group, void *scale_out, void *stream);
 
+/* The linear layer of a quantized weight [SK "HQQLinear layer": the layer computes with the
+ * dequantized weight]: Y[M, N] = X[M, K] . W_r^T, where W_r [N, K] is exactly what
+ * hqq_dequantize reconstructs from an axis-1 quantized weight (rows N, cols K, same packed /
+ * scale / zero / zero_meta layouts); products of binary16 values are accumulated in binary32
+ * (in any order) and Y is rounded to binary16. X: binary16 row-major [M, K], 16-byte aligned;
+ * Y: binary16 row-major [M, N]. M <= 8 streams the packed weight once per call; larger M runs
+ * on the matrix cores. */
+hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *scale,
+                    const void *zero, const void *zero_meta, int64_t N, int64_t K, int nbits,
+                    int group_size, int zero_bits, void *Y, void *stream);
+
 /* Pack n_codes uint8 codes (each < 2^nbits) into the packed layout above; `packed` must be
  * 16-byte aligned and hold hqq_packed_bytes(n_codes, nbits) bytes. Codes >= 2^nbits are
  * masked to their low nbits bits. */

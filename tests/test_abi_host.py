@@ -156,3 +156,20 @@ def test_streamed_entry_points_validate(H):
         H.HQQ_ERR_ARG
     empty = (H.hqq_job * 1)(_job(H, rows=0))
     assert L.hqq_quantize_streamed(empty, 1, None, 0, None, 0, None, None) == H.HQQ_OK
+
+
+def test_gemm_validates(H):
+    L = H.lib()
+    p = [C.c_void_p(a) for a in (0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)]
+    X, P, S, Z, M_, Y = p
+    ok, arg, uns = H.HQQ_OK, H.HQQ_ERR_ARG, H.HQQ_ERR_UNSUPPORTED
+    assert L.hqq_gemm(X, 0, None, None, None, None, 64, 128, 4, 64, 16, None, None) == ok
+    assert L.hqq_gemm(X, -1, P, S, Z, None, 64, 128, 4, 64, 16, Y, None) == arg
+    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 100, 4, 64, 16, Y, None) == arg    # g | K
+    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 128, 5, 64, 16, Y, None) == arg
+    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 128, 4, 8, 16, Y, None) == uns
+    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 128, 4, 64, 12, Y, None) == arg
+    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 128, 4, 64, 8, Y, None) == arg     # no meta
+    assert L.hqq_gemm(None, 4, P, S, Z, None, 64, 128, 4, 64, 16, Y, None) == arg
+    assert L.hqq_gemm(C.c_void_p(0x1008), 4, P, S, Z, None, 64, 128, 4, 64, 16, Y, None) == arg
+    assert L.hqq_gemm(X, 4, C.c_void_p(0x2002), S, Z, None, 64, 130, 3, 10, 16, Y, None) != ok

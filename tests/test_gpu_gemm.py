@@ -1,0 +1,110 @@
+"""The quantized linear layer Y = X . W_r^T on the GPU (through the C ABI) against the
+oracle. Needs an MI355X.
+
+Tolerance, from the arithmetic: W_r is the same binary16 reconstruction on both sides and each
+product of two binary16 values is exact in binary32, so the GPU result differs from the
+binary64 oracle only by the binary32 summation (at most K+1 roundings of partial sums, each
+within 2^-24 of the running magnitude: (K+1)·2^-24·sum|x||w|) and the final rounding to
+binary16 (half an ulp: 2^-11·|y|, or 2^-25 below the normal range)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.conftest import has_gpu
+from tests.gpu_util import u16
+
+pytestmark = pytest.mark.gpu
+
+if has_gpu():
+    from calibration_free_weight_amd import hqq
+
+RNG = np.random.default_rng(4040)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not has_gpu():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def qweight(O, n, k, nbits, g, zero_bits, seed):
+    """Oracle-quantized weight [n, k] (inputs of the GEMM come from the oracle, not the GPU)."""
+    w16 = synth.half_bits(synth.student_t_weights(n, k, seed)).reshape(-1)
+    r = O.quantize(w16, g, nbits, zero_bits=zero_bits)
+    return r
+
+
+def to_dev(a, dt, dev):
+    return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(dev)
+
+
+def run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev):
+    X = to_dev(x16, np.int16, dev).view(m, k)
+    packed = to_dev(r["packed"], np.uint8, dev)
+    scale = to_dev(r["scale"], np.int16, dev)
+    zero = to_dev(r["zero"], np.int16 if zero_bits == 16 else np.uint8, dev)
+    meta = None if zero_bits == 16 else to_dev(r["zero_meta"], np.int16, dev)
+    Y = torch.full((m, n), float("nan"), dtype=torch.float16, device=dev)
+    hqq.hqq_gemm(X, packed, scale, zero, meta, n, k, nbits, g, zero_bits, Y)
+    torch.cuda.synchronize()
+    return u16(Y).view(np.float16).astype(np.float64).reshape(m, n)
+
+
+def check(O, r, x16, y, m, n, k, g, zero_bits, label):
+    ref = O.gemm(x16, r["codes"], r["scale"], r["zero"], r["zero_meta"], n, k, g, zero_bits)
+    w = O.dequantize(r["codes"], r["scale"], r["zero"], r["zero_meta"], g, zero_bits)
+    w = np.abs(w.view(np.float16).astype(np.float64).reshape(n, k))
+    x = np.abs(x16.view(np.float16).astype(np.float64).reshape(m, k))
+    tol = (k + 1) * 2.0 ** -24 * (x @ w.T) + np.maximum(2.0 ** -11 * np.abs(ref), 2.0 ** -25)
+    err = np.abs(y - ref)
+    assert not np.isnan(y).any(), f"{label}: unwritten outputs"
+    assert np.all(err <= tol * (1 + 1e-9)), f"{label}: max err/tol {np.max(err / tol):.3f}"
+    return ref
+
+
+@pytest.mark.parametrize("nbits,g,zero_bits", [(4, 128, 8), (4, 16, 16), (2, 32, 8),
+                                               (3, 64, 16), (8, 16, 8), (1, 64, 16)])
+@pytest.mark.parametrize("m", [1, 3, 8, 9, 64, 100])
+def test_gemm_matches_oracle(O, dev, nbits, g, zero_bits, m):
+    n, k = 200, 1024 + 16 * (g == 16)        # ragged against the 128-wide tiles; K % 64 = 16
+    label = f"gemm m={m} n={n} k={k} nbits={nbits} g={g} zero_bits={zero_bits}"
+    print(label, flush=True)
+    r = qweight(O, n, k, nbits, g, zero_bits, 10 * nbits + g)
+    x16 = synth.half_bits(synth.student_t_weights(m, k, 3 + m)).reshape(-1)
+    x16 = (x16.view(np.float16).astype(np.float32) * 40).astype(np.float16).view(np.uint16)
+    y = run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev)
+    check(O, r, x16, y, m, n, k, g, zero_bits, label)
+
+
+def test_gemm_layer_shape_sampled(O, dev):
+    # a 7B MLP layer shape (N = 11008, K = 4096, 4-bit g128) at decode (M = 1) and prefill
+    # (M = 512) sizes. The GPU quantizes and multiplies the whole layer; the oracle quantizes
+    # the sampled rows from the same weights (binary16 zeros: rows are independent) and
+    # computes the sampled outputs.
+    n, k, nbits, g = 11008, 4096, 4, 128
+    W = synth.student_t_weights(n, k, 77, device=dev)
+    out = hqq.quantize(W, nbits, g, zero_bits=16)
+    torch.cuda.synchronize()
+    rows = np.unique(RNG.integers(0, n, 48))
+    ridx = torch.from_numpy(rows).to(dev)
+    ref_w = O.quantize(u16(W[ridx]).reshape(-1), g, nbits, zero_bits=16)
+    w = O.dequantize(ref_w["codes"], ref_w["scale"], ref_w["zero"], None, g, 16)
+    w = np.abs(w.view(np.float16).astype(np.float64).reshape(rows.size, k))
+    for m in (1, 512):
+        print(f"gemm layer shape m={m}", flush=True)
+        X = synth.student_t_weights(m, k, 900 + m, device=dev).mul_(40)
+        Y = torch.full((m, n), float("nan"), dtype=torch.float16, device=dev)
+        hqq.hqq_gemm(X, out["packed"], out["scale"], out["zero"], None, n, k, nbits, g, 16, Y)
+        torch.cuda.synchronize()
+        ms = np.unique(RNG.integers(0, m, min(m, 16)))
+        midx = torch.from_numpy(ms).to(dev)
+        x16 = u16(X[midx]).reshape(-1)
+        ref = O.gemm(x16, ref_w["codes"], ref_w["scale"], ref_w["zero"], None, rows.size, k, g,
+                     16)
+        y = u16(Y[midx][:, ridx]).view(np.float16).astype(np.float64).reshape(ms.size, rows.size)
+        xa = np.abs(x16.view(np.float16).astype(np.float64).reshape(ms.size, k))
+        tol = (k + 1) * 2.0 ** -24 * (xa @ w.T) + np.maximum(2.0 ** -11 * np.abs(ref), 2.0 ** -25)
+        assert np.all(np.abs(y - ref) <= tol * (1 + 1e-9)), f"m={m}"
+        assert not torch.isnan(Y).any(), f"m={m}: unwritten outputs"
