@@ -24,6 +24,7 @@ namespace {
 typedef uint32_t g4u __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float g_h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t g_f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
@@ -130,13 +131,26 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint16_t *__restrict__ 
             const int64_t k0 = kb + (int64_t)it * 64 * 32;
             if (k0 >= w.K) break;
             load_codes32<NB>(w, n, k0, q[it]);
+            if (w.g_log2 >= 5) {                 // the 32 codes lie in one group
+                const int64_t gi = n * gpr + (k0 >> w.g_log2);
+                const float z = zero_of(w, gi, m0, m1), sv = g_h2f(w.scale[gi]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int64_t kk = k0 + 8 * c < w.K ? k0 + 8 * c : k0;
-                const int64_t gi = n * gpr + (kk >> w.g_log2);
-                zf[it][c] = zero_of(w, gi, m0, m1);
-                sc[it][c] = g_h2f(w.scale[gi]);
-                if constexpr (MB == 1)
+                for (int c = 0; c < 4; ++c) {
+                    zf[it][c] = z;
+                    sc[it][c] = sv;
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t kk = k0 + 8 * c < w.K ? k0 + 8 * c : k0;
+                    const int64_t gi = n * gpr + (kk >> w.g_log2);
+                    zf[it][c] = zero_of(w, gi, m0, m1);
+                    sc[it][c] = g_h2f(w.scale[gi]);
+                }
+            }
+            if constexpr (MB == 1) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
                     xv[it][c] = k0 + 8 * c < w.K ? *reinterpret_cast<const g4u *>(X + k0 + 8 * c)
                                                  : g4u{0, 0, 0, 0};
             }
@@ -149,21 +163,22 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint16_t *__restrict__ 
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if (8 * c >= valid) break;
-                float wf[8];
+                h2 wp[4];                        // binary16 weight pairs
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    wf[i] = g_h2f(g_f2h(((float)q[it][8 * c + i] - zf[it][c]) * sc[it][c]));
+                for (int i = 0; i < 4; ++i)
+                    wp[i] = __builtin_bit_cast(
+                        h2, (uint32_t)g_f2h(((float)q[it][8 * c + 2 * i] - zf[it][c]) * sc[it][c]) |
+                                (uint32_t)g_f2h(((float)q[it][8 * c + 2 * i + 1] - zf[it][c]) * sc[it][c]) << 16);
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
                     if (m >= M) break;
                     const g4u x = MB == 1 ? xv[it][c]
                                           : *reinterpret_cast<const g4u *>(X + (int64_t)m * w.K + k0 + 8 * c);
                     const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+                    // two exact binary16 products per step into the binary32 sum
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float xf = g_h2f((uint16_t)(i & 1 ? xs[i >> 1] >> 16 : xs[i >> 1]));
-                        acc[m] = fmaf(xf, wf[i], acc[m]);   // exact product, binary32 sum
-                    }
+                    for (int i = 0; i < 4; ++i)
+                        acc[m] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, xs[i]), wp[i], acc[m], false);
                 }
             }
         }
