@@ -264,7 +264,8 @@ def gemm_row(specs, outs, dev, stream, reps=5):
     """The quantized linear layers of the stack (hqq_gemm on the 224 quantized weights the
     benchmark just wrote). Decode, M = 1: HBM-bound on the packed weights; the 224 calls are
     captured in a HIP graph (launch gaps would dominate otherwise) and the replay is checked
-    against the eager result. Prefill, M = 512: the matrix-core path, 2*M*N*K flops."""
+    against the eager result. Prefill, M = 512: W_r reconstructed once per call into a
+    workspace, then the binary16 matrix-core GEMM; 2*M*N*K flops."""
     import torch
     from calibration_free_weight_amd import hqq
     kmax = max(s.cols for s in specs)
@@ -274,11 +275,14 @@ def gemm_row(specs, outs, dev, stream, reps=5):
         Ys = [torch.empty(m, s.rows, dtype=torch.float16, device=dev) for s in specs]
 
         Xs = {c: X[:, :c].contiguous() for c in {s.cols for s in specs}}
+        wb = max(hqq.hqq_gemm_workspace_bytes(m, s.rows, s.cols) for s in specs)
+        ws = torch.empty(wb, dtype=torch.uint8, device=dev) if wb else None
 
         def run_all():
             for s, o, Y in zip(specs, outs, Ys):
                 hqq.hqq_gemm(Xs[s.cols], o["packed"], o["scale"], o["zero"], o["zero_meta"],
-                             s.rows, s.cols, s.nbits, s.group_size, s.zero_bits, Y)
+                             s.rows, s.cols, s.nbits, s.group_size, s.zero_bits, Y,
+                             workspace=ws)
         run_all()
         torch.cuda.synchronize()
         eager = [y.clone() for y in Ys]
@@ -309,6 +313,7 @@ def gemm_row(specs, outs, dev, stream, reps=5):
         nbytes = wbytes + sum(m * s.cols * 2 + m * s.rows * 2 for s in specs)
         flops = sum(2.0 * m * s.rows * s.cols for s in specs)
         row = {"m": m, "ms_per_stack": round(ms, 4), "graph": graphed,
+               "workspace_bytes": wb,
                "bytes": nbytes, "flops": flops,
                "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
@@ -319,7 +324,7 @@ def gemm_row(specs, outs, dev, stream, reps=5):
             row.update(bound="mfma", achieved=row["tflops"], peak=2500.0, unit="TFLOP/s",
                        frac=round(row["tflops"] / 2500.0, 4))
         res[f"m{m}"] = row
-        del X, Ys, eager, Xs
+        del X, Ys, eager, Xs, ws
     return res
 
 

@@ -607,9 +607,15 @@ hqq_status hqq_dequantize_scales(const uint8_t *scale_q, const void *scale_meta,
     return HQQ_OK;
 }
 
+size_t hqq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    return hqq::gemm_workspace_bytes(M, N, K);
+}
+
 hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *scale,
                     const void *zero, const void *zero_meta, int64_t N, int64_t K, int nbits,
-                    int group_size, int zero_bits, void *Y, void *stream)
+                    int group_size, int zero_bits, void *Y, void *workspace,
+                    size_t workspace_bytes, void *stream)
 {
     hqq_status st = check_layout(N, K, nbits, group_size, 1, "");
     if (st != HQQ_OK) return st;
@@ -626,11 +632,17 @@ hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *sc
         (zero_bits == 8 && !aligned(zero_meta, 2)))
         return fail(HQQ_ERR_ARG, "binary16 buffers must be 2-byte aligned");
     if (nbits == 3 && !aligned(packed, 4)) return fail(HQQ_ERR_ARG, "packed must be 4-byte aligned");
+    const size_t need = hqq::gemm_workspace_bytes(M, N, K);
+    if (workspace && need > 0 && workspace_bytes < need)
+        return fail(HQQ_ERR_WORKSPACE, "workspace smaller than hqq_gemm_workspace_bytes(M, N, K)");
+    if (workspace && !aligned(workspace, 16))
+        return fail(HQQ_ERR_ARG, "workspace must be 16-byte aligned");
     hipError_t e = hqq::launch_gemm(static_cast<const uint16_t *>(X), M,
                                     static_cast<const uint8_t *>(packed),
                                     static_cast<const uint16_t *>(scale), zero,
                                     static_cast<const uint16_t *>(zero_meta), N, K, nbits,
                                     group_size, zero_bits, static_cast<uint16_t *>(Y),
+                                    need > 0 ? static_cast<uint16_t *>(workspace) : nullptr,
                                     static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(e, "gemm launch");
     g_last_error.clear();

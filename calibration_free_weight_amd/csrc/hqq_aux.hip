@@ -14,7 +14,16 @@ namespace hqq {
 namespace {
 
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-__device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
+// binary32 -> binary16, round to nearest even, of an already rounded binary32 value. The
+// empty asm hides how f was computed: otherwise the compiler folds a binary32 multiply or fma
+// feeding the conversion into one mixed-precision instruction (v_fma_mixlo_f16) that rounds
+// the exact result to binary16 once, which differs from rounding to binary32 first whenever
+// the binary32 value is a binary16 tie.
+__device__ __forceinline__ uint16_t f2h(float f)
+{
+    asm("" : "+v"(f));
+    return __half_as_ushort(__float2half_rn(f));
+}
 
 // ---------------------------------------------------------------------------------------
 // After the solve, per batch: 8-bit zero-points and the 3-bit words shared by two groups.

@@ -5,13 +5,15 @@
 // binary16((q - zero) * scale) in binary32, exactly as hqq_dequantize writes it; products of
 // two binary16 values are exact in binary32 and accumulate in binary32; Y is stored binary16.
 //
-// Two paths:
+// Three paths:
 //  * M <= 8 (decode): one wave per output row streams the row's packed codes (32 per lane per
 //    step), reconstructs them in registers and accumulates every X row against them; a wave
 //    reduction ends the row. HBM-bound on the packed weight.
-//  * larger M: 64 x 128 output tiles per 256-thread block; each K step of 64 stages the X tile
-//    and the reconstructed binary16 W tile in LDS and runs the v_mfma_f32_16x16x32_f16 matrix
-//    cores (each wave a 32 x 64 sub-tile: 2 x 4 accumulators of 16 x 16).
+//  * larger M, fused: 64 x 128 output tiles per 256-thread block; each K step of 64 stages the
+//    X tile and the reconstructed binary16 W tile in LDS and runs the v_mfma_f32_16x16x32_f16
+//    matrix cores (each wave a 32 x 64 sub-tile: 2 x 4 accumulators of 16 x 16).
+//  * M > 64 with a workspace: W_r is written once into the workspace as binary16 and a plain
+//    binary16 MFMA GEMM (double-buffered LDS, XCD-aware tile order) reads it.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -27,7 +29,16 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float g_h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
-__device__ __forceinline__ uint16_t g_f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
+// binary32 -> binary16, round to nearest even, of an already rounded binary32 value. The
+// empty asm hides how f was computed: otherwise the compiler folds a binary32 multiply or fma
+// feeding the conversion into one mixed-precision instruction (v_fma_mixlo_f16) that rounds
+// the exact result to binary16 once, which differs from rounding to binary32 first whenever
+// the binary32 value is a binary16 tie.
+__device__ __forceinline__ uint16_t g_f2h(float f)
+{
+    asm("" : "+v"(f));
+    return __half_as_ushort(__float2half_rn(f));
+}
 
 struct QW {                      // a packed axis-1 quantized weight [N, K]
     const uint8_t *packed;
@@ -107,6 +118,20 @@ __device__ __forceinline__ void recon32(const QW &w, int64_t n, int64_t k0, floa
 // M <= 8: one wave per output row; MB X rows at most (the launch picks 1, 2, 4 or 8).
 // ---------------------------------------------------------------------------------------
 constexpr int kSkinnyM = 8;
+constexpr int kFusedM = 64;      // up to one 64-row block: the fused kernel reconstructs once
+#ifndef HQQ_GEMM_DEPTH
+#define HQQ_GEMM_DEPTH 2
+#endif
+constexpr int kDepth = HQQ_GEMM_DEPTH;   // K steps of loads in flight in the binary16 GEMM
+#ifndef HQQ_GEMM_BM
+#define HQQ_GEMM_BM 0
+#endif
+constexpr int kBM16 = HQQ_GEMM_BM;       // output rows per block of the binary16 GEMM (0: chosen)
+#ifndef HQQ_GEMM_KS
+#define HQQ_GEMM_KS 2
+#endif
+constexpr int kSplitK = HQQ_GEMM_KS;     // wave groups splitting each K step
+constexpr int64_t kMaxWsK = int64_t(1) << 22;   // 32-bit buffer offsets over 128 rows of K
 
 template <int NB, int MB>
 __global__ void __launch_bounds__(256) gemv_kernel(const uint16_t *__restrict__ X, int M, QW w,
@@ -324,11 +349,269 @@ __global__ void __launch_bounds__(256) gemm_mfma_kernel(const uint16_t *__restri
             }
 }
 
+// ---------------------------------------------------------------------------------------
+// Larger M with a workspace: W_r is reconstructed once into binary16 (HBM-bound), then a
+// plain binary16 matrix-core GEMM reads it. The fused kernel above reconstructs each weight
+// tile once per 64-row block of X, which dominates once there are several such blocks.
+// ---------------------------------------------------------------------------------------
+
+// Reconstruction as a flat map: with groups along rows and g | K, code i (row-major) belongs
+// to group i / g, so W_r[i] = binary16((q_i - zero[i/g]) * scale[i/g]) needs no row
+// arithmetic. A unit is 8 consecutive codes (one 16-byte store; g >= 16, so one group); units
+// are lane-contiguous, so each load and store instruction of a wave covers one contiguous
+// range. Each thread takes U units, a grid apart, with all their loads issued first.
+constexpr int kReconU = 4;
+
 template <int NB>
-void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStream_t stream)
+__device__ __forceinline__ void unit_codes(const uint8_t *packed, int64_t u, uint32_t (&q)[8])
+{
+    if constexpr (NB == 3) {                     // ten codes per 32-bit word
+        const uint32_t *wd = reinterpret_cast<const uint32_t *>(packed);
+        const int64_t c0 = u * 8, w0 = c0 / 10;
+        const int j = (int)(c0 - w0 * 10);
+        const uint32_t a = wd[w0], b = j > 2 ? wd[w0 + 1] : 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int p = j + i;
+            q[i] = (p < 10 ? a >> (3 * p) : b >> (3 * (p - 10))) & 7u;
+        }
+    } else {
+        uint32_t lo, hi = 0;                     // the unit's NB bytes
+        if constexpr (NB == 1) lo = packed[u];
+        else if constexpr (NB == 2) lo = reinterpret_cast<const uint16_t *>(packed)[u];
+        else if constexpr (NB == 4) lo = reinterpret_cast<const uint32_t *>(packed)[u];
+        else {
+            const uint2 v = reinterpret_cast<const uint2 *>(packed)[u];
+            lo = v.x;
+            hi = v.y;
+        }
+        constexpr uint32_t mask = (1u << NB) - 1u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            q[i] = NB == 8 ? ((i < 4 ? lo : hi) >> (8 * (i & 3))) & mask : (lo >> (NB * i)) & mask;
+    }
+}
+
+template <int NB>
+__global__ void __launch_bounds__(256) recon_kernel(QW w, int64_t n, uint16_t *__restrict__ Wr)
+{
+    constexpr int U = kReconU;
+    const int64_t units = n >> 3, T = (int64_t)gridDim.x * 256;
+    const float m0 = w.meta ? g_h2f(w.meta[0]) : 0.0f, m1 = w.meta ? g_h2f(w.meta[1]) : 0.0f;
+    for (int64_t u0 = (int64_t)blockIdx.x * 256 + threadIdx.x; u0 < units; u0 += T * U) {
+        uint32_t q[U][8];
+        float zf[U], sc[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t u = u0 + k * T;
+            if (u >= units) break;
+            unit_codes<NB>(w.packed, u, q[k]);
+            const int64_t gi = (u * 8) >> w.g_log2;
+            zf[k] = zero_of(w, gi, m0, m1);
+            sc[k] = g_h2f(w.scale[gi]);
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int64_t u = u0 + k * T;
+            if (u >= units) break;
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                o[i] = (uint32_t)g_f2h(((float)q[k][2 * i] - zf[k]) * sc[k]) |
+                       (uint32_t)g_f2h(((float)q[k][2 * i + 1] - zf[k]) * sc[k]) << 16;
+            *reinterpret_cast<g4u *>(Wr + u * 8) = g4u{o[0], o[1], o[2], o[3]};
+        }
+    }
+}
+
+#ifndef HQQ_GEMM_SWZ
+#define HQQ_GEMM_SWZ 1
+#endif
+// LDS layout of the binary16 GEMM's tiles: rows of BK halves (8 chunks of 16 bytes), chunk c
+// of row r stored at chunk c ^ f(r), f(r) = (r/2) ^ 4*(r%2). A matrix-core operand read
+// (lanes 0..15 read one chunk of rows r0..r0+15) and a row store (8 lanes per row) then touch
+// distinct banks whether the LDS serves 8 or 16 lanes of a 16-byte access per cycle.
+constexpr int kRow16 = HQQ_GEMM_SWZ ? BK : LP;          // row pitch (halves)
+__device__ __forceinline__ int lds_pos(int r, int c)
+{
+    if constexpr (HQQ_GEMM_SWZ) return r * BK + ((c ^ (((r >> 1) ^ ((r & 1) << 2)) & 7)) << 3);
+    else return r * LP + c * 8;
+}
+
+// Y[M, N] = X[M, K] . Wr[N, K]^T, all binary16 row-major, binary32 accumulation.
+// BMT x 128 output tiles per block of 256*KS threads: KS groups of four waves, each wave a
+// BMT/2 x 64 sub-tile; group g takes the 32-wide k slices g, g + KS, ... of every K step of
+// 64, and the groups' sums are added at the end (KS = 2 gives two waves per SIMD for the same
+// LDS traffic, so one wave's LDS and barrier waits overlap the other's matrix-core work).
+// K steps go through two LDS buffers; the global loads run D steps ahead in a ring of
+// register sets (a block is latency-bound on its loads otherwise); each step stores the next
+// step's set into the other LDS buffer (one barrier per step). Blocks are spread so that each
+// XCD takes a contiguous range of tiles, n-major with the row tiles of one weight tile
+// adjacent: that tile is then fetched into one L2.
+template <int BMT, int D, int KS>
+__global__ void __launch_bounds__(256 * KS) gemm_f16_kernel(const uint16_t *__restrict__ X,
+                                                            int64_t M,
+                                                            const uint16_t *__restrict__ Wr,
+                                                            int64_t N, int64_t K,
+                                                            uint16_t *__restrict__ Y)
+{
+    constexpr int NT = 256 * KS;
+    constexpr int TI = BMT / 32;                 // 16-row MFMA tiles per wave
+    constexpr int XL = BMT * BK / 8 / NT;        // 16-byte X chunks per thread per step
+    constexpr int WL = BN * BK / 8 / NT;         // 16-byte W chunks per thread per step
+    static_assert(XL >= 1 && WL >= 1 && BK % (32 * KS) == 0, "tile split");
+    // two buffers of the X tile, then two of the W tile; at the end, group 1's sums
+    constexpr int kLds = 2 * (BMT + BN) * kRow16;
+    static_assert(KS == 1 || 256 * TI * 16 * 4 <= kLds * 2, "reduction fits the LDS");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[kLds];
+    auto xs = [&](int buf) { return lds + buf * BMT * kRow16; };
+    auto ws = [&](int buf) { return lds + 2 * BMT * kRow16 + buf * BN * kRow16; };
+    const int t = threadIdx.x, lane = t & 63, wave = (t >> 6) & 3, grp = t >> 8;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t tiles_m = (M + BMT - 1) / BMT;
+    int64_t b = blockIdx.x;
+    const int64_t per = gridDim.x / 8;
+    if (b < per * 8) b = (b % 8) * per + b / 8;
+    const int64_t m0 = (b % tiles_m) * BMT, n0 = (b / tiles_m) * BN;
+
+    f4 acc[TI][4];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+    // Buffer loads over the block's rows: an offset at or past the record count returns
+    // zeros, so rows past M or N, columns past K and whole steps past the end need no
+    // branches, and every load of the ring stays countable by the wait counters.
+    const uint32_t kOut = 0x80000000u;
+    auto rsrc = [](const uint16_t *base, int64_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0,
+                                                 (int)(bytes < 0x7FFFFFF0 ? bytes : 0x7FFFFFF0),
+                                                 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t rx = rsrc(X + m0 * K, (M - m0) * K * 2);
+    const __amdgpu_buffer_rsrc_t rw = rsrc(Wr + n0 * K, (N - n0) * K * 2);
+    const int col = (t & 7) * 8;                 // the thread's 8 columns of every chunk
+    uint32_t xo[XL], wo[WL];                     // byte offsets of the chunks at k = 0
+#pragma unroll
+    for (int c = 0; c < XL; ++c) xo[c] = (uint32_t)((((t + NT * c) >> 3) * K + col) * 2);
+#pragma unroll
+    for (int c = 0; c < WL; ++c) wo[c] = (uint32_t)((((t + NT * c) >> 3) * K + col) * 2);
+    g4u xr[D][XL], wr[D][WL];
+    auto load = [&](int64_t k0, g4u (&xv)[XL], g4u (&wv)[WL]) {
+        const bool in = col < K - k0;            // k < K implies k + 8 <= K
+        const uint32_t kb = (uint32_t)(k0 * 2);
+#pragma unroll
+        for (int c = 0; c < XL; ++c)
+            xv[c] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xo[c] + kb : kOut, 0, 0);
+#pragma unroll
+        for (int c = 0; c < WL; ++c)
+            wv[c] = __builtin_amdgcn_raw_buffer_load_b128(rw, in ? wo[c] + kb : kOut, 0, 0);
+    };
+    auto store = [&](int buf, const g4u (&xi)[XL], const g4u (&wi)[WL]) {
+#pragma unroll
+        for (int c = 0; c < XL; ++c) {
+            const int idx = t + NT * c;
+            *reinterpret_cast<g4u *>(xs(buf) + lds_pos(idx >> 3, idx & 7)) = xi[c];
+        }
+#pragma unroll
+        for (int c = 0; c < WL; ++c) {
+            const int idx = t + NT * c;
+            *reinterpret_cast<g4u *>(ws(buf) + lds_pos(idx >> 3, idx & 7)) = wi[c];
+        }
+    };
+
+    // Ring invariant at the top of step kt: LDS buffer kt&1 holds step kt; register set
+    // (kt + i) % D holds step kt + i for 1 <= i < D (loads in flight); set kt % D is free.
+    // The loop runs whole rings of D steps: steps past the end hold zeros and add nothing.
+    const int64_t nk = (K + BK - 1) / BK;
+#pragma unroll
+    for (int d = 0; d < D; ++d) load((int64_t)d * BK, xr[d], wr[d]);
+    store(0, xr[0], wr[0]);
+    __syncthreads();
+    for (int64_t kt0 = 0; kt0 < nk; kt0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int64_t kt = kt0 + d;
+            const int cur = (d & 1) ^ (int)(kt0 & 1);   // = kt & 1
+            load((kt + D) * BK, xr[d], wr[d]);
+#pragma unroll
+            for (int s = 0; s < BK / 32 / KS; ++s) {
+                const int ch = (s * KS + grp) * 4 + (lane >> 4);   // the lane's 16-byte chunk
+                h8 a[TI], bv[4];
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+                    a[i] = *reinterpret_cast<const h8 *>(xs(cur) + lds_pos(BMT / 2 * wm + 16 * i + (lane & 15), ch));
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bv[j] = *reinterpret_cast<const h8 *>(ws(cur) + lds_pos(64 * wn + 16 * j + (lane & 15), ch));
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], bv[j], acc[i][j], 0, 0, 0);
+            }
+            store(cur ^ 1, xr[(d + 1) % D], wr[(d + 1) % D]);
+            __syncthreads();
+        }
+    }
+    if constexpr (KS == 2) {
+        // group 1 hands its sums to group 0 through the (now idle) LDS buffers
+        float *red = reinterpret_cast<float *>(lds);
+        const int slot = wave * 64 + lane;
+        if (grp == 1) {
+#pragma unroll
+            for (int i = 0; i < TI; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) red[((i * 4 + j) * 4 + e) * 256 + slot] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][e] += red[((i * 4 + j) * 4 + e) * 256 + slot];
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + BMT / 2 * wm + 16 * i + 4 * (lane >> 4) + e;
+                const int64_t n = n0 + 64 * wn + 16 * j + (lane & 15);
+                if (m < M && n < N) Y[m * N + n] = g_f2h(acc[i][j][e]);
+            }
+}
+
+template <int NB>
+void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t *Wr,
+               hipStream_t stream)
 {
     const dim3 block(256);
-    if (M <= kSkinnyM) {
+    if (M > kFusedM && Wr) {
+        const int64_t n = w.N * w.K;            // a multiple of 16
+        const int64_t per_block = 256 * kReconU;
+        const int64_t rb = (n / 8 + per_block - 1) / per_block;
+        hipLaunchKernelGGL((recon_kernel<NB>), dim3((unsigned)(rb < 65536 ? rb : 65536)), block,
+                           0, stream, w, n, Wr);
+        // 128-row tiles halve the LDS and L2 traffic per flop; 64-row tiles when the larger
+        // ones would not give every CU two blocks
+        const int64_t tn = (w.N + BN - 1) / BN;
+        const bool tall = kBM16 == 128 || (kBM16 == 0 && ((M + 127) / 128) * tn >= 512);
+        if (tall)
+            hipLaunchKernelGGL((gemm_f16_kernel<128, kDepth, kSplitK>),
+                               dim3((unsigned)(((M + 127) / 128) * tn)), dim3(256 * kSplitK), 0,
+                               stream, X, M, Wr, w.N, w.K, Y);
+        else
+            hipLaunchKernelGGL((gemm_f16_kernel<64, kDepth, kSplitK>),
+                               dim3((unsigned)(((M + 63) / 64) * tn)), dim3(256 * kSplitK), 0,
+                               stream, X, M, Wr, w.N, w.K, Y);
+    } else if (M <= kSkinnyM) {
         const dim3 grid((unsigned)((w.N + 3) / 4));
         if (M == 1) hipLaunchKernelGGL((gemv_kernel<NB, 1>), grid, block, 0, stream, X, (int)M, w, Y);
         else if (M == 2) hipLaunchKernelGGL((gemv_kernel<NB, 2>), grid, block, 0, stream, X, (int)M, w, Y);
@@ -342,20 +625,27 @@ void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStream
 
 }  // namespace
 
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= kFusedM || N <= 0 || K <= 0 || K > kMaxWsK) return 0;
+    return ((size_t)N * (size_t)K * 2 + 255) & ~(size_t)255;
+}
+
 hipError_t launch_gemm(const uint16_t *X, int64_t M, const uint8_t *packed, const uint16_t *scale,
                        const void *zero, const uint16_t *zero_meta, int64_t N, int64_t K,
-                       int nbits, int g, int zero_bits, uint16_t *Y, hipStream_t stream)
+                       int nbits, int g, int zero_bits, uint16_t *Y, uint16_t *Wr,
+                       hipStream_t stream)
 {
     if (M == 0 || N == 0) return hipSuccess;
     int lg = 0;
     while ((1 << lg) < g) ++lg;
     const QW w{packed, scale, zero, zero_bits == 8 ? zero_meta : nullptr, N, K, lg, zero_bits};
     switch (nbits) {
-    case 1: launch_nb<1>(X, M, w, Y, stream); break;
-    case 2: launch_nb<2>(X, M, w, Y, stream); break;
-    case 3: launch_nb<3>(X, M, w, Y, stream); break;
-    case 4: launch_nb<4>(X, M, w, Y, stream); break;
-    case 8: launch_nb<8>(X, M, w, Y, stream); break;
+    case 1: launch_nb<1>(X, M, w, Y, Wr, stream); break;
+    case 2: launch_nb<2>(X, M, w, Y, Wr, stream); break;
+    case 3: launch_nb<3>(X, M, w, Y, Wr, stream); break;
+    case 4: launch_nb<4>(X, M, w, Y, Wr, stream); break;
+    case 8: launch_nb<8>(X, M, w, Y, Wr, stream); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

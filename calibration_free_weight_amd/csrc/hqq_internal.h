@@ -73,9 +73,12 @@ bool codes_transpose_fused(int nbits, int64_t R, int64_t C);
 hipError_t launch_transposes(const XTask *tasks, int n, hipStream_t stream);
 
 // Y[M, N] = X[M, K] . W_r^T for a packed axis-1 quantized weight [N, K] (binary16 X, Y).
+// Wr: binary16 [N, K] workspace of gemm_workspace_bytes(M, N, K) bytes, or nullptr
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint16_t *X, int64_t M, const uint8_t *packed, const uint16_t *scale,
                        const void *zero, const uint16_t *zero_meta, int64_t N, int64_t K,
-                       int nbits, int g, int zero_bits, uint16_t *Y, hipStream_t stream);
+                       int nbits, int g, int zero_bits, uint16_t *Y, uint16_t *Wr,
+                       hipStream_t stream);
 
 // 8-bit scales: scale_group a power of two in [8, 512]; buffers 16-byte aligned (meta 4).
 hipError_t launch_scale_requant(const uint16_t *scale, int64_t n, int scale_group, uint8_t *sq,

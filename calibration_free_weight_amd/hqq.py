@@ -18,7 +18,8 @@ HQQ_OK, HQQ_ERR_ARG, HQQ_ERR_UNSUPPORTED, HQQ_ERR_WORKSPACE, HQQ_ERR_DEVICE = ra
 # Functions declared in include/hqq.h (checked by the tests against the header).
 EXPORTS = ("hqq_packed_bytes", "hqq_workspace_bytes", "hqq_quantize", "hqq_quantize_batch",
            "hqq_solve_batch", "hqq_requant_batch", "hqq_quantize_streamed",
-           "hqq_streamed_workspace_bytes", "hqq_dequantize", "hqq_gemm", "hqq_requant_scales",
+           "hqq_streamed_workspace_bytes", "hqq_dequantize", "hqq_gemm",
+           "hqq_gemm_workspace_bytes", "hqq_requant_scales",
            "hqq_dequantize_scales", "hqq_pack", "hqq_unpack", "hqq_status_string",
            "hqq_last_error")
 
@@ -67,7 +68,10 @@ def lib():
         L.hqq_dequantize.restype = i32
         L.hqq_dequantize.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp]
         L.hqq_gemm.restype = i32
-        L.hqq_gemm.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp, vp]
+        L.hqq_gemm.argtypes = [vp, i64, vp, vp, vp, vp, i64, i64, i32, i32, i32, vp, vp,
+                               C.c_size_t, vp]
+        L.hqq_gemm_workspace_bytes.restype = C.c_size_t
+        L.hqq_gemm_workspace_bytes.argtypes = [i64, i64, i64]
         L.hqq_requant_scales.restype = i32
         L.hqq_requant_scales.argtypes = [vp, i64, i32, vp, vp, vp]
         L.hqq_dequantize_scales.restype = i32
@@ -184,11 +188,19 @@ def hqq_dequantize(packed, scale, zero, zero_meta, rows, cols, nbits, group_size
 
 
 def hqq_gemm(X, packed, scale, zero, zero_meta, N, K, nbits, group_size, zero_bits, Y,
-             stream=None) -> None:
-    """Y[M, N] = X[M, K] . W_r^T for a packed axis-1 quantized weight [N, K]."""
+             workspace=None, stream=None) -> None:
+    """Y[M, N] = X[M, K] . W_r^T for a packed axis-1 quantized weight [N, K]; `workspace`
+    (optional, at least hqq_gemm_workspace_bytes(M, N, K) bytes) selects the reconstruct-once
+    path for M > 64."""
     M = X.shape[0]
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hqq_gemm(_p(X), M, _p(packed), _p(scale), _p(zero), _p(zero_meta), N, K,
-                          nbits, group_size, zero_bits, _p(Y), _stream(stream)))
+                          nbits, group_size, zero_bits, _p(Y), _p(workspace), wb,
+                          _stream(stream)))
+
+
+def hqq_gemm_workspace_bytes(M, N, K) -> int:
+    return int(lib().hqq_gemm_workspace_bytes(M, N, K))
 
 
 def hqq_requant_scales(scale, n, scale_group, scale_q, scale_meta, stream=None) -> None:

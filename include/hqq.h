@@ -178,10 +178,20 @@ hqq_status hqq_dequantize_scales(const uint8_t *scale_q, const void *scale_meta,
  * scale / zero / zero_meta layouts); products of binary16 values are accumulated in binary32
  * (in any order) and Y is rounded to binary16. X: binary16 row-major [M, K], 16-byte aligned;
  * Y: binary16 row-major [M, N]. M <= 8 streams the packed weight once per call; larger M runs
- * on the matrix cores. */
+ * on the matrix cores.
+ * workspace (optional, device, 16-byte aligned, caller-owned): with M > 64 and at least
+ * hqq_gemm_workspace_bytes(M, N, K) bytes, W_r is reconstructed once into it and a plain
+ * binary16 GEMM reads it (much faster for large M); NULL keeps the single fused kernel, which
+ * reconstructs each weight tile once per 64 rows of X. A non-NULL workspace that is too small
+ * is HQQ_ERR_WORKSPACE. Its contents are scratch; calls that share one race. */
 hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *scale,
                     const void *zero, const void *zero_meta, int64_t N, int64_t K, int nbits,
-                    int group_size, int zero_bits, void *Y, void *stream);
+                    int group_size, int zero_bits, void *Y, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for hqq_gemm's reconstruct-once path: 2*N*K rounded up to 256 for M > 64,
+ * else 0 (no workspace is used). */
+size_t hqq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Pack n_codes uint8 codes (each < 2^nbits) into the packed layout above; `packed` must be
  * 16-byte aligned and hold hqq_packed_bytes(n_codes, nbits) bytes. Codes >= 2^nbits are

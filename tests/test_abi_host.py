@@ -163,13 +163,24 @@ def test_gemm_validates(H):
     p = [C.c_void_p(a) for a in (0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000)]
     X, P, S, Z, M_, Y = p
     ok, arg, uns = H.HQQ_OK, H.HQQ_ERR_ARG, H.HQQ_ERR_UNSUPPORTED
-    assert L.hqq_gemm(X, 0, None, None, None, None, 64, 128, 4, 64, 16, None, None) == ok
-    assert L.hqq_gemm(X, -1, P, S, Z, None, 64, 128, 4, 64, 16, Y, None) == arg
-    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 100, 4, 64, 16, Y, None) == arg    # g | K
-    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 128, 5, 64, 16, Y, None) == arg
-    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 128, 4, 8, 16, Y, None) == uns
-    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 128, 4, 64, 12, Y, None) == arg
-    assert L.hqq_gemm(X, 4, P, S, Z, None, 64, 128, 4, 64, 8, Y, None) == arg     # no meta
-    assert L.hqq_gemm(None, 4, P, S, Z, None, 64, 128, 4, 64, 16, Y, None) == arg
-    assert L.hqq_gemm(C.c_void_p(0x1008), 4, P, S, Z, None, 64, 128, 4, 64, 16, Y, None) == arg
-    assert L.hqq_gemm(X, 4, C.c_void_p(0x2002), S, Z, None, 64, 130, 3, 10, 16, Y, None) != ok
+
+    def gm(*a, ws=None, wb=0):                   # no workspace unless given, default stream
+        return L.hqq_gemm(*a, ws, wb, None)
+    assert gm(X, 0, None, None, None, None, 64, 128, 4, 64, 16, None) == ok
+    assert gm(X, -1, P, S, Z, None, 64, 128, 4, 64, 16, Y) == arg
+    assert gm(X, 4, P, S, Z, None, 64, 100, 4, 64, 16, Y) == arg      # g | K
+    assert gm(X, 4, P, S, Z, None, 64, 128, 5, 64, 16, Y) == arg
+    assert gm(X, 4, P, S, Z, None, 64, 128, 4, 8, 16, Y) == uns
+    assert gm(X, 4, P, S, Z, None, 64, 128, 4, 64, 12, Y) == arg
+    assert gm(X, 4, P, S, Z, None, 64, 128, 4, 64, 8, Y) == arg       # no meta
+    assert gm(None, 4, P, S, Z, None, 64, 128, 4, 64, 16, Y) == arg
+    assert gm(C.c_void_p(0x1008), 4, P, S, Z, None, 64, 128, 4, 64, 16, Y) == arg
+    assert gm(X, 4, C.c_void_p(0x2002), S, Z, None, 64, 130, 3, 10, 16, Y) != ok
+    # the optional workspace of the reconstruct-once path (M > 64)
+    need = L.hqq_gemm_workspace_bytes(65, 64, 128)
+    assert need == 64 * 128 * 2 and L.hqq_gemm_workspace_bytes(64, 64, 128) == 0
+    assert L.hqq_gemm_workspace_bytes(100, 11008, 4096) == 11008 * 4096 * 2
+    assert L.hqq_gemm_workspace_bytes(100, 3, 16) == 256                 # rounded up
+    a = (X, 65, P, S, Z, None, 64, 128, 4, 64, 16, Y)
+    assert gm(*a, ws=C.c_void_p(0x7000), wb=need - 1) == H.HQQ_ERR_WORKSPACE
+    assert gm(*a, ws=C.c_void_p(0x7008), wb=need) == arg                # 16-byte alignment

@@ -40,14 +40,18 @@ def to_dev(a, dt, dev):
     return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(dev)
 
 
-def run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev):
+def run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev, workspace=False):
     X = to_dev(x16, np.int16, dev).view(m, k)
     packed = to_dev(r["packed"], np.uint8, dev)
     scale = to_dev(r["scale"], np.int16, dev)
     zero = to_dev(r["zero"], np.int16 if zero_bits == 16 else np.uint8, dev)
     meta = None if zero_bits == 16 else to_dev(r["zero_meta"], np.int16, dev)
     Y = torch.full((m, n), float("nan"), dtype=torch.float16, device=dev)
-    hqq.hqq_gemm(X, packed, scale, zero, meta, n, k, nbits, g, zero_bits, Y)
+    ws = None
+    if workspace:
+        wb = hqq.hqq_gemm_workspace_bytes(m, n, k)
+        ws = torch.full((max(wb, 1),), 0x7E, dtype=torch.uint8, device=dev)
+    hqq.hqq_gemm(X, packed, scale, zero, meta, n, k, nbits, g, zero_bits, Y, workspace=ws)
     torch.cuda.synchronize()
     return u16(Y).view(np.float16).astype(np.float64).reshape(m, n)
 
@@ -69,13 +73,32 @@ def check(O, r, x16, y, m, n, k, g, zero_bits, label):
 @pytest.mark.parametrize("m", [1, 3, 8, 9, 64, 100])
 def test_gemm_matches_oracle(O, dev, nbits, g, zero_bits, m):
     n, k = 200, 1024 + 16 * (g == 16)        # ragged against the 128-wide tiles; K % 64 = 16
-    label = f"gemm m={m} n={n} k={k} nbits={nbits} g={g} zero_bits={zero_bits}"
-    print(label, flush=True)
     r = qweight(O, n, k, nbits, g, zero_bits, 10 * nbits + g)
     x16 = synth.half_bits(synth.student_t_weights(m, k, 3 + m)).reshape(-1)
     x16 = (x16.view(np.float16).astype(np.float32) * 40).astype(np.float16).view(np.uint16)
-    y = run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev)
-    check(O, r, x16, y, m, n, k, g, zero_bits, label)
+    for ws in (False, True) if m > 64 else (False,):
+        label = f"gemm m={m} n={n} k={k} nbits={nbits} g={g} zero_bits={zero_bits} ws={ws}"
+        print(label, flush=True)
+        y = run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev, workspace=ws)
+        check(O, r, x16, y, m, n, k, g, zero_bits, label)
+
+
+@pytest.mark.parametrize("m,n,k", [(65, 128, 16), (130, 129, 48), (257, 300, 2064),
+                                   (200, 1, 32), (512, 256, 4096), (520, 8200, 272)])
+def test_gemm_workspace_path_shapes(O, dev, m, n, k):
+    # the reconstruct-once path: ragged M and N against the 64 x 128 and 128 x 128 tiles (the
+    # last shape has enough tiles for the taller ones), K below one 64-step and with a 16- or
+    # 48-wide tail, a single output column, grids not a multiple of the 8 XCDs; the fused path
+    # on the same inputs must agree with the oracle too
+    nbits, g, zero_bits = 4, 16, 8
+    r = qweight(O, n, k, nbits, g, zero_bits, 5 + m + n + k)
+    x16 = synth.half_bits(synth.student_t_weights(m, k, 17 + m)).reshape(-1)
+    x16 = (x16.view(np.float16).astype(np.float32) * 40).astype(np.float16).view(np.uint16)
+    for ws in (True, False):
+        label = f"gemm shape m={m} n={n} k={k} ws={ws}"
+        print(label, flush=True)
+        y = run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev, workspace=ws)
+        check(O, r, x16, y, m, n, k, g, zero_bits, label)
 
 
 def test_gemm_layer_shape_sampled(O, dev):
@@ -92,11 +115,16 @@ def test_gemm_layer_shape_sampled(O, dev):
     ref_w = O.quantize(u16(W[ridx]).reshape(-1), g, nbits, zero_bits=16)
     w = O.dequantize(ref_w["codes"], ref_w["scale"], ref_w["zero"], None, g, 16)
     w = np.abs(w.view(np.float16).astype(np.float64).reshape(rows.size, k))
-    for m in (1, 512):
-        print(f"gemm layer shape m={m}", flush=True)
+    for m, use_ws in ((1, False), (512, False), (512, True)):
+        print(f"gemm layer shape m={m} workspace={use_ws}", flush=True)
         X = synth.student_t_weights(m, k, 900 + m, device=dev).mul_(40)
         Y = torch.full((m, n), float("nan"), dtype=torch.float16, device=dev)
-        hqq.hqq_gemm(X, out["packed"], out["scale"], out["zero"], None, n, k, nbits, g, 16, Y)
+        ws = None
+        if use_ws:
+            ws = torch.empty(hqq.hqq_gemm_workspace_bytes(m, n, k), dtype=torch.uint8,
+                             device=dev)
+        hqq.hqq_gemm(X, out["packed"], out["scale"], out["zero"], None, n, k, nbits, g, 16, Y,
+                     workspace=ws)
         torch.cuda.synchronize()
         ms = np.unique(RNG.integers(0, m, min(m, 16)))
         midx = torch.from_numpy(ms).to(dev)
@@ -108,3 +136,33 @@ def test_gemm_layer_shape_sampled(O, dev):
         tol = (k + 1) * 2.0 ** -24 * (xa @ w.T) + np.maximum(2.0 ** -11 * np.abs(ref), 2.0 ** -25)
         assert np.all(np.abs(y - ref) <= tol * (1 + 1e-9)), f"m={m}"
         assert not torch.isnan(Y).any(), f"m={m}: unwritten outputs"
+
+
+def test_reconstruction_ties_bit_exact(O, dev):
+    # weights whose binary32 reconstruction is a binary16 tie that a merged (single) rounding
+    # would resolve the other way (8-bit zeros: the zero is a full binary32 value). With X the
+    # identity, Y = W_r^T exactly on every path: hqq_dequantize, the decode kernel (M <= 8),
+    # the fused matrix-core kernel and the reconstruct-once path (M = 128)
+    from tests import ties
+    step, base, g, k = 0.0633, -1.014, 16, 128
+    q, zq, s = ties.dequant_ties(32 * (k // g), 21, step, base)
+    n = q.size // (k // g)
+    meta = np.array([np.float16(step), np.float16(base)]).view(np.uint16)
+    codes = np.repeat(q, g)
+    ref = O.dequantize(codes, s.view(np.uint16), zq, meta, g, 8).view(np.float16).reshape(n, k)
+    packed = to_dev(O.pack(codes, 4), np.uint8, dev)
+    scale, zero, zmeta = to_dev(s, np.int16, dev), to_dev(zq, np.uint8, dev), to_dev(meta, np.int16, dev)
+    Wr = torch.empty(n, k, dtype=torch.float16, device=dev)
+    hqq.hqq_dequantize(packed, scale, zero, zmeta, n, k, 4, g, 1, 8, Wr)
+    torch.cuda.synchronize()
+    assert np.array_equal(Wr.cpu().numpy(), ref), "hqq_dequantize"
+    eye = torch.eye(k, dtype=torch.float16, device=dev)
+    for m, use_ws in ((1, False), (8, False), (128, False), (128, True)):
+        print(f"ties m={m} workspace={use_ws}", flush=True)
+        Y = torch.full((m, n), float("nan"), dtype=torch.float16, device=dev)
+        ws = torch.empty(max(hqq.hqq_gemm_workspace_bytes(m, n, k), 1), dtype=torch.uint8,
+                         device=dev) if use_ws else None
+        hqq.hqq_gemm(eye[:m].contiguous(), packed, scale, zero, zmeta, n, k, 4, g, 8, Y,
+                     workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y.cpu().numpy(), ref[:, :m].T), f"m={m} workspace={use_ws}"

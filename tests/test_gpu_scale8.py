@@ -140,3 +140,19 @@ def test_g16_s_variant_end_to_end(O, dev):
     assert np.array_equal(u16(back), rback)
     rW = O.dequantize(ref["codes"], rback, ref["zero"], ref["zero_meta"], g, 8)
     assert np.array_equal(u16(Wr), rW)
+
+
+def test_scale_dequant_ties_bit_exact(O, dev):
+    # runs whose binary32 fma(q, step, base) is a binary16 tie that a merged (single) rounding
+    # would resolve the other way: the read-back must round to binary32 first, as the oracle
+    from tests import ties
+    q, st, bs = ties.scale_dequant_ties(64, 22)
+    group = 8
+    meta = np.stack([st, bs], axis=1).reshape(-1).view(np.uint16)
+    codes = np.repeat(q, group)
+    ref = O.scale_dequant(codes, meta, group=group)
+    out = torch.empty(codes.size, dtype=torch.int16, device=dev)
+    hqq.hqq_dequantize_scales(torch.from_numpy(codes).to(dev),
+                              torch.from_numpy(meta.view(np.int16)).to(dev), codes.size, group, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(out), ref)
