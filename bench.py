@@ -260,6 +260,38 @@ def host_stream_row(specs, weights, dev, stream, reps=3):
             "overlap": round(copy_ms / ms, 4)}
 
 
+def dequant_row(specs, outs, dev, stream, reps=5):
+    """hqq_dequantize (the layer's dequantize()) on the 224 quantized weights the benchmark
+    just wrote: reads the packed codes, scales and 8-bit zeros, writes binary16 W_r; HBM-bound.
+    One output buffer of the largest tensor's size serves every call."""
+    import torch
+    from calibration_free_weight_amd import hqq
+    out = torch.empty(max(s.rows * s.cols for s in specs), dtype=torch.float16, device=dev)
+
+    def run_all():
+        for s, o in zip(specs, outs):
+            hqq.hqq_dequantize(o["packed"], o["scale"], o["zero"], o["zero_meta"], s.rows,
+                               s.cols, s.nbits, s.group_size, 1, s.zero_bits,
+                               out[:s.rows * s.cols])
+    run_all()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run_all()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = sum(o["packed"].numel() + o["scale"].numel() * 2 +
+                 o["zero"].numel() * o["zero"].element_size() + 2 * s.rows * s.cols
+                 for s, o in zip(specs, outs))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del out
+    return {"variant": "hqq_dequantize of every quantized weight of the stack (axis 1)",
+            "ms_per_stack": round(ms, 4), "bytes": nbytes, "bound": "hbm",
+            "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def gemm_row(specs, outs, dev, stream, reps=5):
     """The quantized linear layers of the stack (hqq_gemm on the 224 quantized weights the
     benchmark just wrote). Decode, M = 1: HBM-bound on the packed weights; the 224 calls are
@@ -471,6 +503,8 @@ def main():
     if args.workload == 2:
         log("bench: axis 0")
         result["next_rows"]["axis0"] = axis0_row(specs, weights, dev, stream, solve_ms)
+        log("bench: dequantize")
+        result["next_rows"]["dequant"] = dequant_row(specs, outs, dev, stream)
         log("bench: quantized linear layers")
         result["next_rows"]["gemm"] = gemm_row(specs, outs, dev, stream)
         log("bench: host streaming")

@@ -551,12 +551,20 @@ hqq_status hqq_dequantize(const void *packed, const void *scale, const void *zer
     if (!aligned(scale, 2) || !aligned(W_out, 2) || (zero_bits == 16 && !aligned(zero, 2)) ||
         (zero_bits == 8 && !aligned(zero_meta, 2)))
         return fail(HQQ_ERR_ARG, "binary16 buffers must be 2-byte aligned");
-    hipError_t e = hqq::launch_dequant(static_cast<const uint8_t *>(packed),
-                                       static_cast<const uint16_t *>(scale), zero,
-                                       static_cast<const uint16_t *>(zero_meta), n, nbits,
-                                       group_size, zero_bits, cols, axis,
-                                       static_cast<uint16_t *>(W_out),
-                                       static_cast<hipStream_t>(stream));
+    // the flat, coalesced kernel when the alignments allow, else the element-wise one
+    const bool flat = hqq::recon_fits(packed, nbits, cols, axis, W_out);
+    hipError_t e =
+        flat ? hqq::launch_recon(static_cast<const uint8_t *>(packed),
+                                 static_cast<const uint16_t *>(scale), zero,
+                                 static_cast<const uint16_t *>(zero_meta), rows, cols, nbits,
+                                 group_size, zero_bits, axis, static_cast<uint16_t *>(W_out),
+                                 static_cast<hipStream_t>(stream))
+             : hqq::launch_dequant(static_cast<const uint8_t *>(packed),
+                                   static_cast<const uint16_t *>(scale), zero,
+                                   static_cast<const uint16_t *>(zero_meta), n, nbits,
+                                   group_size, zero_bits, cols, axis,
+                                   static_cast<uint16_t *>(W_out),
+                                   static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(e, "dequantize launch");
     g_last_error.clear();
     return HQQ_OK;

@@ -392,23 +392,39 @@ __device__ __forceinline__ void unit_codes(const uint8_t *packed, int64_t u, uin
     }
 }
 
-template <int NB>
-__global__ void __launch_bounds__(256) recon_kernel(QW w, int64_t n, uint16_t *__restrict__ Wr)
+// AX0: groups run down columns instead (hqq_dequantize of an axis-0 weight with cols a
+// multiple of 8): the unit's 8 codes lie in one row and belong to 8 consecutive groups of the
+// [rows/g, cols] per-group arrays. NT: nontemporal (streaming) stores, for an output that is
+// not read again soon (hqq_dequantize; the GEMM's workspace is read right after and is
+// better left in the caches).
+template <int NB, bool AX0, bool NT>
+__global__ void __launch_bounds__(256) recon_kernel(QW w, int64_t n, int64_t cols,
+                                                   uint16_t *__restrict__ Wr)
 {
     constexpr int U = kReconU;
+    constexpr int ZS = AX0 ? 8 : 1;              // scale/zero pairs per unit
     const int64_t units = n >> 3, T = (int64_t)gridDim.x * 256;
     const float m0 = w.meta ? g_h2f(w.meta[0]) : 0.0f, m1 = w.meta ? g_h2f(w.meta[1]) : 0.0f;
     for (int64_t u0 = (int64_t)blockIdx.x * 256 + threadIdx.x; u0 < units; u0 += T * U) {
         uint32_t q[U][8];
-        float zf[U], sc[U];
+        float zf[U][ZS], sc[U][ZS];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const int64_t u = u0 + k * T;
             if (u >= units) break;
             unit_codes<NB>(w.packed, u, q[k]);
-            const int64_t gi = (u * 8) >> w.g_log2;
-            zf[k] = zero_of(w, gi, m0, m1);
-            sc[k] = g_h2f(w.scale[gi]);
+            int64_t gi;
+            if constexpr (AX0) {
+                const int64_t row = (u * 8) / cols;
+                gi = (row >> w.g_log2) * cols + (u * 8 - row * cols);
+            } else {
+                gi = (u * 8) >> w.g_log2;
+            }
+#pragma unroll
+            for (int e = 0; e < ZS; ++e) {
+                zf[k][e] = zero_of(w, gi + e, m0, m1);
+                sc[k][e] = g_h2f(w.scale[gi + e]);
+            }
         }
 #pragma unroll
         for (int k = 0; k < U; ++k) {
@@ -416,12 +432,31 @@ __global__ void __launch_bounds__(256) recon_kernel(QW w, int64_t n, uint16_t *_
             if (u >= units) break;
             uint32_t o[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[i] = (uint32_t)g_f2h(((float)q[k][2 * i] - zf[k]) * sc[k]) |
-                       (uint32_t)g_f2h(((float)q[k][2 * i + 1] - zf[k]) * sc[k]) << 16;
-            *reinterpret_cast<g4u *>(Wr + u * 8) = g4u{o[0], o[1], o[2], o[3]};
+            for (int i = 0; i < 4; ++i) {
+                const int a = AX0 ? 2 * i : 0, b = AX0 ? 2 * i + 1 : 0;
+                o[i] = (uint32_t)g_f2h(((float)q[k][2 * i] - zf[k][a]) * sc[k][a]) |
+                       (uint32_t)g_f2h(((float)q[k][2 * i + 1] - zf[k][b]) * sc[k][b]) << 16;
+            }
+            const g4u v{o[0], o[1], o[2], o[3]};
+            if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<g4u *>(Wr + u * 8));
+            else *reinterpret_cast<g4u *>(Wr + u * 8) = v;
         }
     }
+}
+
+template <int NB>
+void launch_recon_nb(const QW &w, int64_t n, int64_t cols, int axis, bool nt, uint16_t *out,
+                     hipStream_t stream)
+{
+    const int64_t per_block = 256 * kReconU;
+    const int64_t rb = (n / 8 + per_block - 1) / per_block;
+    const dim3 grid((unsigned)(rb < 65536 ? rb : 65536)), block(256);
+    if (axis == 0)
+        hipLaunchKernelGGL((recon_kernel<NB, true, true>), grid, block, 0, stream, w, n, cols, out);
+    else if (nt)
+        hipLaunchKernelGGL((recon_kernel<NB, false, true>), grid, block, 0, stream, w, n, cols, out);
+    else
+        hipLaunchKernelGGL((recon_kernel<NB, false, false>), grid, block, 0, stream, w, n, cols, out);
 }
 
 #ifndef HQQ_GEMM_SWZ
@@ -594,11 +629,7 @@ void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t 
 {
     const dim3 block(256);
     if (M > kFusedM && Wr) {
-        const int64_t n = w.N * w.K;            // a multiple of 16
-        const int64_t per_block = 256 * kReconU;
-        const int64_t rb = (n / 8 + per_block - 1) / per_block;
-        hipLaunchKernelGGL((recon_kernel<NB>), dim3((unsigned)(rb < 65536 ? rb : 65536)), block,
-                           0, stream, w, n, Wr);
+        launch_recon_nb<NB>(w, w.N * w.K, w.K, 1, false, Wr, stream);   // N*K: a multiple of 16
         // 128-row tiles halve the LDS and L2 traffic per flop; 64-row tiles when the larger
         // ones would not give every CU two blocks
         const int64_t tn = (w.N + BN - 1) / BN;
@@ -624,6 +655,34 @@ void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t 
 }
 
 }  // namespace
+
+bool recon_fits(const void *packed, int nbits, int64_t cols, int axis, const void *out)
+{
+    const uintptr_t p = reinterpret_cast<uintptr_t>(packed);
+    const int word = nbits == 8 ? 8 : nbits == 3 ? 4 : nbits;   // bytes per 8-code load
+    return (reinterpret_cast<uintptr_t>(out) & 15) == 0 && (p & (word - 1)) == 0 &&
+           (axis == 1 || cols % 8 == 0);
+}
+
+hipError_t launch_recon(const uint8_t *packed, const uint16_t *scale, const void *zero,
+                        const uint16_t *zero_meta, int64_t rows, int64_t cols, int nbits, int g,
+                        int zero_bits, int axis, uint16_t *out, hipStream_t stream)
+{
+    const int64_t n = rows * cols;
+    if (n == 0) return hipSuccess;
+    int lg = 0;
+    while ((1 << lg) < g) ++lg;
+    const QW w{packed, scale, zero, zero_bits == 8 ? zero_meta : nullptr, rows, cols, lg, zero_bits};
+    switch (nbits) {
+    case 1: launch_recon_nb<1>(w, n, cols, axis, true, out, stream); break;
+    case 2: launch_recon_nb<2>(w, n, cols, axis, true, out, stream); break;
+    case 3: launch_recon_nb<3>(w, n, cols, axis, true, out, stream); break;
+    case 4: launch_recon_nb<4>(w, n, cols, axis, true, out, stream); break;
+    case 8: launch_recon_nb<8>(w, n, cols, axis, true, out, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {

@@ -73,6 +73,13 @@ bool codes_transpose_fused(int nbits, int64_t R, int64_t C);
 hipError_t launch_transposes(const XTask *tasks, int n, hipStream_t stream);
 
 // Y[M, N] = X[M, K] . W_r^T for a packed axis-1 quantized weight [N, K] (binary16 X, Y).
+// Flat reconstruction of a packed weight into binary16 (hqq_dequantize's fast path): needs
+// recon_fits (16-byte aligned output, packed aligned to one 8-code load, and for axis 0 cols
+// a multiple of 8); n = rows*cols is then a multiple of 8.
+bool recon_fits(const void *packed, int nbits, int64_t cols, int axis, const void *out);
+hipError_t launch_recon(const uint8_t *packed, const uint16_t *scale, const void *zero,
+                        const uint16_t *zero_meta, int64_t rows, int64_t cols, int nbits, int g,
+                        int zero_bits, int axis, uint16_t *out, hipStream_t stream);
 // Wr: binary16 [N, K] workspace of gemm_workspace_bytes(M, N, K) bytes, or nullptr
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint16_t *X, int64_t M, const uint8_t *packed, const uint16_t *scale,
