@@ -118,6 +118,10 @@ __device__ __forceinline__ void recon32(const QW &w, int64_t n, int64_t k0, floa
 // M <= 8: one wave per output row; MB X rows at most (the launch picks 1, 2, 4 or 8).
 // ---------------------------------------------------------------------------------------
 constexpr int kSkinnyM = 8;
+#ifndef HQQ_GEMV_ROWS
+#define HQQ_GEMV_ROWS 2
+#endif
+constexpr int kGemvRows = HQQ_GEMV_ROWS;  // rows per wave of the M = 1 decode kernel
 constexpr int kFusedM = 64;      // up to one 64-row block: the fused kernel reconstructs once
 #ifndef HQQ_GEMM_DEPTH
 #define HQQ_GEMM_DEPTH 2
@@ -215,6 +219,165 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint16_t *__restrict__ 
 #pragma unroll
         for (int off = 32; off >= 1; off /= 2) v += __shfl_xor(v, off);
         if (lane == 0) Y[(int64_t)m * w.N + n] = g_f2h(v);
+    }
+}
+
+// M <= 8, bit widths 1, 2, 4, 8 with K*nbits a multiple of 32 and a 4-byte aligned packed
+// buffer: each wave takes R consecutive rows (R > 1 for one X row: the lane's X values are
+// loaded once and used for every row). A lane takes chunks of 32 codes, 2048 codes apart.
+// Everything is read with buffer loads from wave-uniform bases; an offset past the end of a
+// buffer reads zero, so chunks past K (X = 0: they add nothing) and rows past N need no
+// branches. The codes of a 32-bit word are split into byte planes (one mask per plane) and
+// each byte converted by v_cvt_f32_ubyte.
+template <int NB>
+__device__ __forceinline__ void plane_codes(const uint32_t (&wd)[NB], float (&c)[32])
+{
+    constexpr int P = 8 / NB;                   // planes per word
+    constexpr uint32_t m = ((1u << NB) - 1u) * 0x01010101u;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            uint32_t pl = (wd[i] >> (NB * p)) & m;
+            if constexpr (NB < 8) asm("" : "+v"(pl));   // keep the plane: one byte convert per code
+#pragma unroll
+            for (int b = 0; b < 4; ++b) c[i * (32 / NB) + b * P + p] = (float)((pl >> (8 * b)) & 0xFFu);
+        }
+}
+
+template <int NB>
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t (&wd)[NB])
+{
+    if constexpr (NB == 1) {
+        wd[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else if constexpr (NB == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        wd[0] = v[0];
+        wd[1] = v[1];
+    } else if constexpr (NB == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wd[i] = v[i];
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            wd[i] = v[i];
+            wd[4 + i] = u[i];
+        }
+    }
+}
+
+// A buffer resource over [base, base + bytes) (clamped below 2^31). Base and size must be
+// wave-uniform; both pass through readfirstlane, because 64-bit compares and selects on the
+// way can leave them in VGPRs, and a resource in VGPRs makes every load through it a
+// waterfall loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    const int nr = __builtin_amdgcn_readfirstlane((int)(bytes < 0x7FFFFFF0 ? bytes : 0x7FFFFFF0));
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(hi << 32 | lo), (short)0,
+                                             nr, 0x00020000);
+}
+
+template <int NB, int MB, int R, int ZB>
+__global__ void __launch_bounds__(256) gemv2_kernel(const uint16_t *__restrict__ X, int M, QW w,
+                                                    uint16_t *__restrict__ Y)
+{
+    constexpr int zb = ZB / 8;                   // bytes per stored zero
+    constexpr uint32_t kOut = 0x80000000u;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+    if (n0 >= w.N) return;                       // whole wave
+    const int64_t rows = w.N - n0 < R ? w.N - n0 : R;
+    const int64_t rb = w.K * NB / 8;             // packed bytes per row (a multiple of 4)
+    const int64_t gpr = w.K >> w.g_log2;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(w.packed + n0 * rb, rows * rb);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(w.scale + n0 * gpr, rows * gpr * 2);
+    const __amdgpu_buffer_rsrc_t rz =
+        make_rsrc(static_cast<const uint8_t *>(w.zero) + n0 * gpr * zb, rows * gpr * zb);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, (int64_t)M * w.K * 2);
+    const float m0 = w.meta ? g_h2f(w.meta[0]) : 0.0f, m1 = w.meta ? g_h2f(w.meta[1]) : 0.0f;
+    const int gsh = w.g_log2;
+    float acc[MB][R];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
+
+    constexpr int IT = MB >= 4 ? 1 : 2;          // chunks per lane in flight
+    const int64_t steps = (w.K + 2047) >> 11;    // chunks of the row per lane (some past K)
+    for (int64_t j0 = 0; j0 < steps; j0 += IT) {
+        uint32_t wd[IT][R][NB];
+        uint16_t sv[IT][R][2], zv[IT][R][2];
+        g4u xv[IT][MB][4];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int64_t k = ((j0 + it) * 64 + lane) * 32;
+            const bool in = k < w.K;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                load_words<NB>(rp, in ? (uint32_t)(r * rb + k * NB / 8) : kOut, wd[it][r]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {       // the groups of codes 0-15 and 16-31
+                    const uint32_t gi = (uint32_t)(r * gpr + ((k + 16 * h) >> gsh));
+                    sv[it][r][h] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, in ? gi * 2 : kOut, 0, 0);
+                    if constexpr (zb == 2)
+                        zv[it][r][h] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rz, in ? gi * 2 : kOut, 0, 0);
+                    else
+                        zv[it][r][h] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b8(rz, in ? gi : kOut, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const uint32_t off = m < M && in ? (uint32_t)((m * w.K + k + 8 * c) * 2) : kOut;
+                    xv[it][m][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+                }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float c[32];
+                plane_codes<NB>(wd[it][r], c);
+                float zf[2], sc[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if constexpr (zb == 2) zf[h] = g_h2f(zv[it][r][h]);
+                    else zf[h] = fmaf((float)zv[it][r][h], m0, m1);
+                    sc[h] = g_h2f(sv[it][r][h]);
+                }
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {      // pairs of codes
+                    const int h = q >> 3;
+                    const h2 wp = __builtin_bit_cast(
+                        h2, (uint32_t)g_f2h((c[2 * q] - zf[h]) * sc[h]) |
+                                (uint32_t)g_f2h((c[2 * q + 1] - zf[h]) * sc[h]) << 16);
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) {
+                        const uint32_t xw = xv[it][m][q >> 2][q & 3];
+                        acc[m][r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, xw), wp, acc[m][r], false);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+        if (m >= M) break;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float v = acc[m][r];
+#pragma unroll
+            for (int off = 32; off >= 1; off /= 2) v += __shfl_xor(v, off);
+            if (lane == 0 && r < rows) Y[(int64_t)m * w.N + n0 + r] = g_f2h(v);
+        }
     }
 }
 
@@ -623,6 +786,22 @@ __global__ void __launch_bounds__(256 * KS) gemm_f16_kernel(const uint16_t *__re
             }
 }
 
+template <int NB, int ZB>
+void launch_gemv2(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStream_t stream)
+{
+    const dim3 block(256);
+    if (M == 1) {
+        constexpr int R = kGemvRows;
+        const dim3 grid((unsigned)((w.N + 4 * R - 1) / (4 * R)));
+        hipLaunchKernelGGL((gemv2_kernel<NB, 1, R, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
+        return;
+    }
+    const dim3 grid((unsigned)((w.N + 3) / 4));
+    if (M == 2) hipLaunchKernelGGL((gemv2_kernel<NB, 2, 1, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
+    else if (M <= 4) hipLaunchKernelGGL((gemv2_kernel<NB, 4, 1, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
+    else hipLaunchKernelGGL((gemv2_kernel<NB, 8, 1, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
+}
+
 template <int NB>
 void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t *Wr,
                hipStream_t stream)
@@ -642,6 +821,11 @@ void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t 
             hipLaunchKernelGGL((gemm_f16_kernel<64, kDepth, kSplitK>),
                                dim3((unsigned)(((M + 63) / 64) * tn)), dim3(256 * kSplitK), 0,
                                stream, X, M, Wr, w.N, w.K, Y);
+    } else if (M <= kSkinnyM && NB != 3 && (w.K * NB) % 32 == 0 &&
+               (reinterpret_cast<uintptr_t>(w.packed) & 3) == 0 && M * w.K * 2 < 0x7FFFFFF0 &&
+               4 * (w.K * NB / 8) < 0x7FFFFFF0) {
+        if (w.zero_bits == 8) launch_gemv2<NB, 8>(X, M, w, Y, stream);
+        else launch_gemv2<NB, 16>(X, M, w, Y, stream);
     } else if (M <= kSkinnyM) {
         const dim3 grid((unsigned)((w.N + 3) / 4));
         if (M == 1) hipLaunchKernelGGL((gemv_kernel<NB, 1>), grid, block, 0, stream, X, (int)M, w, Y);
