@@ -337,7 +337,7 @@ __global__ void __launch_bounds__(256) scale_dequant_kernel(const uint8_t *__res
 // 64-element tile rows.
 // ---------------------------------------------------------------------------------------
 enum XSub { kXGen16, kXWhole16, kXGen8, kXCodes1, kXCodes2, kXCodes4, kXCodes8, kXWide1,
-            kXWide2, kXWide4, kXWide8 };
+            kXWide2, kXWide4, kXWide8, kXNib4 };
 
 struct XTaskDev {
     const void *src;
@@ -434,6 +434,66 @@ __device__ void xtile_codes(const uint8_t *__restrict__ src, int64_t R, int64_t 
     }
 }
 
+// 4-bit codes with R and C multiples of 8 (the usual case): 128 x 128 output tiles. Each
+// thread loads an 8 x 8 block of codes as eight 32-bit words (one per source row), transposes
+// it in registers in three swap stages (16-, 8- and 4-bit fields), and writes the eight
+// output words to LDS; the output rows then leave as 16-byte stores (4-byte ones when C is
+// not a multiple of 32). A wave's loads are 64-byte runs of four source rows.
+__device__ __forceinline__ void swap_fields(uint32_t &a, uint32_t &b, int sh, uint32_t keep)
+{
+    const uint32_t na = (a & keep) | ((b << sh) & ~keep);
+    const uint32_t nb = ((a >> sh) & keep) | (b & ~keep);
+    a = na;
+    b = nb;
+}
+
+__device__ void xtile_nib4(const uint8_t *__restrict__ src, int64_t R, int64_t C,
+                           uint8_t *__restrict__ dst, int64_t r0, int64_t c0, uint32_t *tile)
+{
+    constexpr int P = 17;                       // LDS row pitch in words (16 + 1)
+    const int t = threadIdx.x, rb = t & 15, cb = t >> 4;
+    const int64_t r = r0 + rb * 8, c = c0 + cb * 8;
+    uint32_t w[8];
+    if (r < R && c < C) {                       // R, C multiples of 8: blocks are whole
+        const uint32_t *s32 = reinterpret_cast<const uint32_t *>(src);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = s32[((c + j) * R + r) >> 3];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w[j] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) swap_fields(w[j], w[j + 4], 16, 0x0000FFFFu);
+#pragma unroll
+    for (int j = 0; j < 8; j += 4) {
+        swap_fields(w[j], w[j + 2], 8, 0x00FF00FFu);
+        swap_fields(w[j + 1], w[j + 3], 8, 0x00FF00FFu);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) swap_fields(w[j], w[j + 1], 4, 0x0F0F0F0Fu);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[(rb * 8 + i) * P + cb] = w[i];   // output row r + i
+    __syncthreads();
+    const bool wide = C % 32 == 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int u = t + 256 * h, rr = u >> 2, q = u & 3;
+        const int64_t orow = r0 + rr, oc = c0 + 32 * q;
+        if (orow >= R || oc >= C) continue;
+        uint32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = tile[rr * P + 4 * q + k];
+        uint32_t *d32 = reinterpret_cast<uint32_t *>(dst + ((orow * C + oc) >> 1));
+        if (wide) {
+            *reinterpret_cast<uint4 *>(d32) = uint4{v[0], v[1], v[2], v[3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (oc + 8 * k < C) d32[k] = v[k];
+        }
+    }
+}
+
 __global__ void __launch_bounds__(256) xpose_kernel(XArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint16_t lds[64 * 68];
@@ -445,9 +505,11 @@ __global__ void __launch_bounds__(256) xpose_kernel(XArgs a)
             else hi = mid - 1;
         }
         const XTaskDev T = a.t[lo];
-        // tiles cover the output for codes ([R, C]) and the input otherwise ([R, C] -> [C, R])
-        const int64_t lt = tile - T.tile0, tc = (T.C + 63) / 64;
-        const int64_t r0 = (lt / tc) * 64, c0 = (lt % tc) * 64;
+        // tiles cover the output for codes ([R, C]) and the input otherwise ([R, C] -> [C, R]);
+        // 128 x 128 for 4-bit codes in whole 8 x 8 blocks, 64 x 64 otherwise
+        const int ts = T.sub == kXNib4 ? 128 : 64;
+        const int64_t lt = tile - T.tile0, tc = (T.C + ts - 1) / ts;
+        const int64_t r0 = (lt / tc) * ts, c0 = (lt % tc) * ts;
         const uint8_t *s8 = static_cast<const uint8_t *>(T.src);
         uint8_t *d8 = static_cast<uint8_t *>(T.dst);
         auto t8 = reinterpret_cast<uint8_t (*)[65]>(lds);
@@ -470,6 +532,7 @@ __global__ void __launch_bounds__(256) xpose_kernel(XArgs a)
         case kXWide1: xtile_codes<1, true>(s8, T.R, T.C, d8, r0, c0, t8); break;
         case kXWide2: xtile_codes<2, true>(s8, T.R, T.C, d8, r0, c0, t8); break;
         case kXWide4: xtile_codes<4, true>(s8, T.R, T.C, d8, r0, c0, t8); break;
+        case kXNib4: xtile_nib4(s8, T.R, T.C, d8, r0, c0, reinterpret_cast<uint32_t *>(lds)); break;
         default: xtile_codes<8, true>(s8, T.R, T.C, d8, r0, c0, t8); break;
         }
         __syncthreads();                        // the tile buffer is reused by the next tile
@@ -581,8 +644,12 @@ hipError_t launch_transposes(const XTask *tasks, int n, hipStream_t stream)
                                   al(t.src, 4) && al(t.dst, 4);
                 const int lg = t.nbits == 1 ? 0 : t.nbits == 2 ? 1 : t.nbits == 4 ? 2 : 3;
                 d.sub = (wide ? kXWide1 : kXCodes1) + lg;
+                if (t.nbits == 4 && t.R % 8 == 0 && t.C % 8 == 0 && al(t.src, 4) &&
+                    al(t.dst, t.C % 32 == 0 ? 16 : 4))
+                    d.sub = kXNib4;
             }
-            tiles += ((t.R + 63) / 64) * ((t.C + 63) / 64);
+            const int ts = d.sub == kXNib4 ? 128 : 64;
+            tiles += ((t.R + ts - 1) / ts) * ((t.C + ts - 1) / ts);
             a.t[a.n++] = d;
         }
         a.tiles = tiles;
