@@ -336,7 +336,11 @@ __global__ void __launch_bounds__(256) gemv2_kernel(const uint16_t *__restrict__
             for (int m = 0; m < MB; ++m)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const uint32_t off = m < M && in ? (uint32_t)((m * w.K + k + 8 * c) * 2) : kOut;
+                    // each 8-code piece masked on its own: with K % 32 == 16 a chunk's second
+                    // half lies past the row, and its X must read zero (the weights there
+                    // may belong to the next row)
+                    const bool inx = m < M && k + 8 * c < w.K;
+                    const uint32_t off = inx ? (uint32_t)((m * w.K + k + 8 * c) * 2) : kOut;
                     xv[it][m][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
                 }
         }

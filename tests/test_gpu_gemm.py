@@ -69,7 +69,8 @@ def check(O, r, x16, y, m, n, k, g, zero_bits, label):
 
 
 @pytest.mark.parametrize("nbits,g,zero_bits", [(4, 128, 8), (4, 16, 16), (2, 32, 8),
-                                               (3, 64, 16), (8, 16, 8), (1, 64, 16)])
+                                               (3, 64, 16), (8, 16, 8), (1, 64, 16),
+                                               (1, 16, 8)])
 @pytest.mark.parametrize("m", [1, 3, 8, 9, 64, 100])
 def test_gemm_matches_oracle(O, dev, nbits, g, zero_bits, m):
     n, k = 200, 1024 + 16 * (g == 16)        # ragged against the 128-wide tiles; K % 64 = 16
@@ -81,6 +82,32 @@ def test_gemm_matches_oracle(O, dev, nbits, g, zero_bits, m):
         print(label, flush=True)
         y = run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev, workspace=ws)
         check(O, r, x16, y, m, n, k, g, zero_bits, label)
+
+
+@pytest.mark.parametrize("nbits,g,zero_bits", [(4, 16, 8), (8, 32, 16), (2, 16, 16)])
+def test_gemm_decode_ragged(O, dev, nbits, g, zero_bits):
+    # the decode kernels on ragged shapes: odd N (a wave's second row missing), one row,
+    # K below one chunk of 32 codes per lane, between chunks, and past one 2048-code sweep
+    # (with g = 16, K % 32 == 16: a lane's last chunk ends half past the row);
+    # packed buffers offset by 4 bytes (still word-aligned) and by 1 byte (the fallback)
+    for m in (1, 2, 5, 8):
+        for n, k in ((1, g), (3, 3 * g), (201, 2048 + g), (7, 4096 + g)):
+            r = qweight(O, n, k, nbits, g, zero_bits, 31 * n + k + nbits)
+            x16 = synth.half_bits(synth.student_t_weights(m, k, 7 + m + k)).reshape(-1)
+            for shift in (0, 4, 1):
+                label = f"decode m={m} n={n} k={k} nbits={nbits} g={g} zb={zero_bits} shift={shift}"
+                print(label, flush=True)
+                X = to_dev(x16, np.int16, dev).view(m, k)
+                pk = torch.zeros(r["packed"].size + 16, dtype=torch.uint8, device=dev)
+                pk[shift:shift + r["packed"].size] = to_dev(r["packed"], np.uint8, dev)
+                scale = to_dev(r["scale"], np.int16, dev)
+                zero = to_dev(r["zero"], np.int16 if zero_bits == 16 else np.uint8, dev)
+                meta = None if zero_bits == 16 else to_dev(r["zero_meta"], np.int16, dev)
+                Y = torch.full((m, n), float("nan"), dtype=torch.float16, device=dev)
+                hqq.hqq_gemm(X, pk[shift:], scale, zero, meta, n, k, nbits, g, zero_bits, Y)
+                torch.cuda.synchronize()
+                y = u16(Y).view(np.float16).astype(np.float64).reshape(m, n)
+                check(O, r, x16, y, m, n, k, g, zero_bits, label)
 
 
 @pytest.mark.parametrize("m,n,k", [(65, 128, 16), (130, 129, 48), (257, 300, 2064),
