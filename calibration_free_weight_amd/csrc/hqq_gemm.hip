@@ -118,11 +118,18 @@ __device__ __forceinline__ void recon32(const QW &w, int64_t n, int64_t k0, floa
 // M <= 8: one wave per output row; MB X rows at most (the launch picks 1, 2, 4 or 8).
 // ---------------------------------------------------------------------------------------
 constexpr int kSkinnyM = 8;
+#ifndef HQQ_SKINNY_LO
+#define HQQ_SKINNY_LO 8
+#endif
+constexpr int kSkinnyLo = HQQ_SKINNY_LO;  // M above this (up to 64): the matrix-core skinny kernel
 #ifndef HQQ_GEMV_ROWS
 #define HQQ_GEMV_ROWS 2
 #endif
 constexpr int kGemvRows = HQQ_GEMV_ROWS;  // rows per wave of the M = 1 decode kernel
-constexpr int kFusedM = 64;      // up to one 64-row block: the fused kernel reconstructs once
+#ifndef HQQ_FUSED_M
+#define HQQ_FUSED_M 64
+#endif
+constexpr int kFusedM = HQQ_FUSED_M;   // up to one 64-row block: the fused kernel reconstructs once
 #ifndef HQQ_GEMM_DEPTH
 #define HQQ_GEMM_DEPTH 2
 #endif
@@ -790,6 +797,180 @@ __global__ void __launch_bounds__(256 * KS) gemm_f16_kernel(const uint16_t *__re
             }
 }
 
+// 8 < M <= 64: the weight streams once and the matrix cores take the products. A block owns
+// 16 weight rows (N) and all of M (MT tiles of 16 rows); its ST waves take the 32-wide K steps
+// w, w + ST, ... and add their sums through LDS at the end, in wave order. Per step a lane
+// reconstructs 8 consecutive codes of its row (exactly the v_mfma_f32_16x16x32_f16 B fragment
+// it holds) and loads its X fragments from L2. Loads run D steps ahead in a ring of raw slots
+// (code words, scale, zero, X); the loop runs whole rings. Rows past N and steps past K read
+// clamped (valid) units: past K their X reads zero through the buffer resource, past N their
+// outputs are never stored, so the loads need no branches.
+template <int NB>
+struct RawUnit {                                 // the 32-bit words holding 8 codes
+    static constexpr int W = NB == 3 || NB == 8 ? 2 : 1;
+    uint32_t w[W];
+    uint32_t j;                                  // 3-bit: position of the first code in w[0]
+};
+
+template <int NB>
+__device__ __forceinline__ void raw_unit(const uint8_t *packed, int64_t u, int64_t n_words,
+                                         RawUnit<NB> &r)
+{
+    if constexpr (NB == 3) {
+        const uint32_t *wd = reinterpret_cast<const uint32_t *>(packed);
+        const int64_t c0 = u * 8, w0 = c0 / 10;
+        r.j = (uint32_t)(c0 - w0 * 10);
+        r.w[0] = wd[w0];
+        r.w[1] = wd[w0 + 1 < n_words ? w0 + 1 : w0];
+    } else if constexpr (NB == 8) {
+        const uint2 v = reinterpret_cast<const uint2 *>(packed)[u];
+        r.w[0] = v.x;
+        r.w[1] = v.y;
+    } else if constexpr (NB == 4) {
+        r.w[0] = reinterpret_cast<const uint32_t *>(packed)[u];
+    } else if constexpr (NB == 2) {
+        r.w[0] = reinterpret_cast<const uint16_t *>(packed)[u];
+    } else {
+        r.w[0] = packed[u];
+    }
+}
+
+template <int NB>
+__device__ __forceinline__ void raw_codes(const RawUnit<NB> &r, float (&c)[8])
+{
+    if constexpr (NB == 3) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t p = r.j + i;
+            c[i] = (float)((p < 10 ? r.w[0] >> (3 * p) : r.w[1] >> (3 * (p - 10))) & 7u);
+        }
+    } else if constexpr (NB == 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = (float)((r.w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    } else {
+        constexpr int P = 8 / NB;                // planes; byte b of plane p: code b*P + p
+        constexpr uint32_t m = ((1u << NB) - 1u) * 0x01010101u;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            uint32_t pl = (r.w[0] >> (NB * p)) & m;
+            asm("" : "+v"(pl));                  // one byte convert per code
+#pragma unroll
+            for (int b = 0; b < 8 / P; ++b) c[b * P + p] = (float)((pl >> (8 * b)) & 0xFFu);
+        }
+    }
+}
+
+template <int NB, int MT, int ZB>
+struct SkinnySlot {
+    RawUnit<NB> u;
+    uint32_t sv, zv;                             // raw binary16 scale; raw zero
+    g4u xa[MT];
+};
+
+template <int NB, int MT, int ZB>
+__global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__restrict__ X,
+                                                          int64_t M, QW w,
+                                                          uint16_t *__restrict__ Y)
+{
+    constexpr uint32_t kOut = 0x80000000u;
+    constexpr int ST = 8, D = 4;                 // waves per block; steps of loads in flight
+    __shared__ float red[(ST - 1) * MT * 4 * 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t nr = n0 + (lane & 15) < w.N ? n0 + (lane & 15) : w.N - 1;   // clamped row
+    const int kl = 8 * (lane >> 4);              // the lane's 8 k within a step
+    const int64_t gpr = w.K >> w.g_log2;
+    const int64_t n_words = (w.N * w.K + 9) / 10;   // 3-bit words
+    const float m0 = w.meta ? g_h2f(w.meta[0]) : 0.0f, m1 = w.meta ? g_h2f(w.meta[1]) : 0.0f;
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, M * w.K * 2);
+    uint32_t xrow[MT];                           // byte offsets of the lane's X rows (clamped)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m = 16 * mt + (lane & 15) < M ? 16 * mt + (lane & 15) : M - 1;
+        xrow[mt] = (uint32_t)(m * w.K * 2);
+    }
+    f4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t steps = (w.K + 31) >> 5;
+    using Slot = SkinnySlot<NB, MT, ZB>;
+    auto load = [&](int64_t s, Slot &r) {
+        const int64_t k = s * 32 + kl;
+        const bool in = s < steps && k < w.K;
+        const int64_t kc = in ? k : 0;
+        raw_unit<NB>(w.packed, (nr * w.K + kc) >> 3, n_words, r.u);
+        const int64_t gi = nr * gpr + (kc >> w.g_log2);
+        r.sv = w.scale[gi];
+        if constexpr (ZB == 16) r.zv = static_cast<const uint16_t *>(w.zero)[gi];
+        else r.zv = static_cast<const uint8_t *>(w.zero)[gi];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            r.xa[mt] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xrow[mt] + (uint32_t)(k * 2) : kOut, 0, 0);
+    };
+    auto step = [&](const Slot &r) {
+        float c[8];
+        raw_codes<NB>(r.u, c);
+        const float sc = g_h2f((uint16_t)r.sv);
+        const float zf = ZB == 16 ? g_h2f((uint16_t)r.zv) : fmaf((float)r.zv, m0, m1);
+        uint32_t bw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            bw[i] = (uint32_t)g_f2h((c[2 * i] - zf) * sc) | (uint32_t)g_f2h((c[2 * i + 1] - zf) * sc) << 16;
+        const h8 b = __builtin_bit_cast(h8, g4u{bw[0], bw[1], bw[2], bw[3]});
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, r.xa[mt]), b, acc[mt], 0, 0, 0);
+    };
+    Slot ring[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(wave + (int64_t)d * ST, ring[d]);
+    for (int64_t s0 = wave; s0 < steps; s0 += (int64_t)D * ST) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {            // steps past the end add zeros
+            step(ring[d]);
+            load(s0 + (int64_t)(d + D) * ST, ring[d]);
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[(((wave - 1) * MT + mt) * 4 + e) * 64 + lane] = acc[mt][e];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+    const int64_t n = n0 + (lane & 15);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = acc[mt][e];
+#pragma unroll
+            for (int v2 = 0; v2 < ST - 1; ++v2) v += red[((v2 * MT + mt) * 4 + e) * 64 + lane];
+            const int64_t m = 16 * mt + 4 * (lane >> 4) + e;
+            if (m < M && n < w.N) Y[m * w.N + n] = g_f2h(v);
+        }
+}
+
+template <int NB, int ZB>
+void launch_skinny_zb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((w.N + 15) / 16)), block(512);
+    if (M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<NB, 1, ZB>), grid, block, 0, stream, X, M, w, Y);
+    else if (M <= 32) hipLaunchKernelGGL((gemm_skinny_kernel<NB, 2, ZB>), grid, block, 0, stream, X, M, w, Y);
+    else if (M <= 48) hipLaunchKernelGGL((gemm_skinny_kernel<NB, 3, ZB>), grid, block, 0, stream, X, M, w, Y);
+    else hipLaunchKernelGGL((gemm_skinny_kernel<NB, 4, ZB>), grid, block, 0, stream, X, M, w, Y);
+}
+
+template <int NB>
+void launch_skinny(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStream_t stream)
+{
+    if (w.zero_bits == 8) launch_skinny_zb<NB, 8>(X, M, w, Y, stream);
+    else launch_skinny_zb<NB, 16>(X, M, w, Y, stream);
+}
+
 template <int NB, int ZB>
 void launch_gemv2(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStream_t stream)
 {
@@ -825,6 +1006,9 @@ void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t 
             hipLaunchKernelGGL((gemm_f16_kernel<64, kDepth, kSplitK>),
                                dim3((unsigned)(((M + 63) / 64) * tn)), dim3(256 * kSplitK), 0,
                                stream, X, M, Wr, w.N, w.K, Y);
+    } else if (M > kSkinnyLo && M <= 64 && M * w.K * 2 < 0x7FFFFFF0 &&
+               (reinterpret_cast<uintptr_t>(w.packed) & (NB == 8 ? 7 : NB == 1 ? 0 : NB == 2 ? 1 : 3)) == 0) {
+        launch_skinny<NB>(X, M, w, Y, stream);
     } else if (M <= kSkinnyM && NB != 3 && (w.K * NB) % 32 == 0 &&
                (reinterpret_cast<uintptr_t>(w.packed) & 3) == 0 && M * w.K * 2 < 0x7FFFFFF0 &&
                4 * (w.K * NB / 8) < 0x7FFFFFF0) {

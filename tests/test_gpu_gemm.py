@@ -110,6 +110,22 @@ def test_gemm_decode_ragged(O, dev, nbits, g, zero_bits):
                 check(O, r, x16, y, m, n, k, g, zero_bits, label)
 
 
+@pytest.mark.parametrize("nbits,g,zero_bits", [(4, 16, 8), (3, 32, 16), (8, 16, 16), (1, 64, 8)])
+def test_gemm_skinny_ragged(O, dev, nbits, g, zero_bits):
+    # the matrix-core skinny kernel (8 < M <= 64): one to four 16-row M tiles, N below, at and
+    # past one 16-row block, K of one 32-wide step (three of the block's four waves idle),
+    # a few steps, and a half step at the end
+    for m in (9, 17, 33, 48, 64):
+        for n, k in ((15, g), (16, 3 * g), (17, 64 + g), (200, 4096 + g)):
+            label = f"skinny m={m} n={n} k={k} nbits={nbits} g={g} zb={zero_bits}"
+            print(label, flush=True)
+            r = qweight(O, n, k, nbits, g, zero_bits, 17 * n + k + nbits)
+            x16 = synth.half_bits(synth.student_t_weights(m, k, 5 + m + k)).reshape(-1)
+            x16 = (x16.view(np.float16).astype(np.float32) * 40).astype(np.float16).view(np.uint16)
+            y = run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev)
+            check(O, r, x16, y, m, n, k, g, zero_bits, label)
+
+
 @pytest.mark.parametrize("m,n,k", [(65, 128, 16), (130, 129, 48), (257, 300, 2064),
                                    (200, 1, 32), (512, 256, 4096), (520, 8200, 272)])
 def test_gemm_workspace_path_shapes(O, dev, m, n, k):
