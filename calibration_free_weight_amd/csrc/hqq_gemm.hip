@@ -5,15 +5,18 @@
 // binary16((q - zero) * scale) in binary32, exactly as hqq_dequantize writes it; products of
 // two binary16 values are exact in binary32 and accumulate in binary32; Y is stored binary16.
 //
-// Three paths:
-//  * M <= 8 (decode): one wave per output row streams the row's packed codes (32 per lane per
-//    step), reconstructs them in registers and accumulates every X row against them; a wave
-//    reduction ends the row. HBM-bound on the packed weight.
-//  * larger M, fused: 64 x 128 output tiles per 256-thread block; each K step of 64 stages the
-//    X tile and the reconstructed binary16 W tile in LDS and runs the v_mfma_f32_16x16x32_f16
-//    matrix cores (each wave a 32 x 64 sub-tile: 2 x 4 accumulators of 16 x 16).
+// Paths by M:
+//  * M = 1 (decode): a wave takes two output rows and streams their packed codes (32 per lane
+//    per chunk), reconstructs them in registers and accumulates the X row against them with
+//    v_dot2; a wave reduction ends each row.
+//  * 2 <= M <= 64 (skinny): the weight streams once; a block owns 16 weight rows, its waves
+//    split K, and each lane reconstructs its v_mfma_f32_16x16x32_f16 B fragment per step.
 //  * M > 64 with a workspace: W_r is written once into the workspace as binary16 and a plain
 //    binary16 MFMA GEMM (double-buffered LDS, XCD-aware tile order) reads it.
+//  * M > 64 without one: the skinny kernel on slices of 64 rows.
+//  * Packed buffers the fast kernels cannot read word-wise (unaligned): the original kernels,
+//    one wave per output row for M <= 8 and, above that, 64 x 128 output tiles per block that
+//    stage the X tile and the reconstructed binary16 W tile in LDS for the matrix cores.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -119,17 +122,14 @@ __device__ __forceinline__ void recon32(const QW &w, int64_t n, int64_t k0, floa
 // ---------------------------------------------------------------------------------------
 constexpr int kSkinnyM = 8;
 #ifndef HQQ_SKINNY_LO
-#define HQQ_SKINNY_LO 8
+#define HQQ_SKINNY_LO 1
 #endif
 constexpr int kSkinnyLo = HQQ_SKINNY_LO;  // M above this (up to 64): the matrix-core skinny kernel
 #ifndef HQQ_GEMV_ROWS
 #define HQQ_GEMV_ROWS 2
 #endif
 constexpr int kGemvRows = HQQ_GEMV_ROWS;  // rows per wave of the M = 1 decode kernel
-#ifndef HQQ_FUSED_M
-#define HQQ_FUSED_M 64
-#endif
-constexpr int kFusedM = HQQ_FUSED_M;   // up to one 64-row block: the fused kernel reconstructs once
+constexpr int kWsM = 64;         // the reconstruct-once path (with a workspace) above this M
 #ifndef HQQ_GEMM_DEPTH
 #define HQQ_GEMM_DEPTH 2
 #endif
@@ -797,12 +797,13 @@ __global__ void __launch_bounds__(256 * KS) gemm_f16_kernel(const uint16_t *__re
             }
 }
 
-// 8 < M <= 64: the weight streams once and the matrix cores take the products. A block owns
+// 2 <= M <= 64: the weight streams once and the matrix cores take the products. A block owns
 // 16 weight rows (N) and all of M (MT tiles of 16 rows); its ST waves take the 32-wide K steps
 // w, w + ST, ... and add their sums through LDS at the end, in wave order. Per step a lane
 // reconstructs 8 consecutive codes of its row (exactly the v_mfma_f32_16x16x32_f16 B fragment
-// it holds) and loads its X fragments from L2. Loads run D steps ahead in a ring of raw slots
-// (code words, scale, zero, X); the loop runs whole rings. Rows past N and steps past K read
+// it holds) with its X fragments. Loads run D steps ahead in a ring of raw slots (code words,
+// scale, zero, X), loaded in a coalescing lane order and moved to the fragment lanes by
+// ds_bpermute when used; the loop runs whole rings. Rows past N and steps past K read
 // clamped (valid) units: past K their X reads zero through the buffer resource, past N their
 // outputs are never stored, so the loads need no branches.
 template <int NB>
@@ -878,16 +879,21 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t n0 = (int64_t)blockIdx.x * 16;
-    const int64_t nr = n0 + (lane & 15) < w.N ? n0 + (lane & 15) : w.N - 1;   // clamped row
-    const int kl = 8 * (lane >> 4);              // the lane's 8 k within a step
+    // MFMA fragment layout: lane t holds row t % 16, k-piece t / 16 (8 k) of a step. Loads
+    // use lane l = 4 * row + piece instead, so 4 neighbouring lanes read one contiguous run
+    // (the fragment layout puts neighbours in different rows, and the texture addresser
+    // then handles almost every lane as its own access); ds_bpermute moves the data over.
+    const int lr = lane >> 2, lp = lane & 3;      // loading lane's row and piece
+    const int src = ((lane & 15) * 4 + (lane >> 4)) * 4;   // byte address of the source lane
+    const int64_t nl = n0 + lr < w.N ? n0 + lr : w.N - 1;   // loading row (clamped)
     const int64_t gpr = w.K >> w.g_log2;
     const int64_t n_words = (w.N * w.K + 9) / 10;   // 3-bit words
     const float m0 = w.meta ? g_h2f(w.meta[0]) : 0.0f, m1 = w.meta ? g_h2f(w.meta[1]) : 0.0f;
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(X, M * w.K * 2);
-    uint32_t xrow[MT];                           // byte offsets of the lane's X rows (clamped)
+    uint32_t xrow[MT];                           // byte offsets of the loading lane's X rows
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int64_t m = 16 * mt + (lane & 15) < M ? 16 * mt + (lane & 15) : M - 1;
+        const int64_t m = 16 * mt + lr < M ? 16 * mt + lr : M - 1;
         xrow[mt] = (uint32_t)(m * w.K * 2);
     }
     f4 acc[MT];
@@ -897,19 +903,29 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
     const int64_t steps = (w.K + 31) >> 5;
     using Slot = SkinnySlot<NB, MT, ZB>;
     auto load = [&](int64_t s, Slot &r) {
-        const int64_t k = s * 32 + kl;
-        const bool in = s < steps && k < w.K;
-        const int64_t kc = in ? k : 0;
-        raw_unit<NB>(w.packed, (nr * w.K + kc) >> 3, n_words, r.u);
-        const int64_t gi = nr * gpr + (kc >> w.g_log2);
+        const int64_t kx = s * 32 + 8 * lp;      // loading lane's k
+        const bool inx = s < steps && kx < w.K;
+        const int64_t kc = inx ? kx : 0;
+        raw_unit<NB>(w.packed, (nl * w.K + kc) >> 3, n_words, r.u);
+        const int64_t gi = nl * gpr + (kc >> w.g_log2);
         r.sv = w.scale[gi];
         if constexpr (ZB == 16) r.zv = static_cast<const uint16_t *>(w.zero)[gi];
         else r.zv = static_cast<const uint8_t *>(w.zero)[gi];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            r.xa[mt] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? xrow[mt] + (uint32_t)(k * 2) : kOut, 0, 0);
+            r.xa[mt] = __builtin_amdgcn_raw_buffer_load_b128(rx, inx ? xrow[mt] + (uint32_t)(kx * 2) : kOut, 0, 0);
     };
-    auto step = [&](const Slot &r) {
+    auto perm = [&](uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v); };
+    auto step = [&](const Slot &r0) {
+        Slot r;                                  // the fragment lane's codes and X
+#pragma unroll
+        for (int i = 0; i < RawUnit<NB>::W; ++i) r.u.w[i] = perm(r0.u.w[i]);
+        if constexpr (NB == 3) r.u.j = perm(r0.u.j);
+        r.sv = perm(r0.sv);
+        r.zv = perm(r0.zv);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            r.xa[mt] = g4u{perm(r0.xa[mt].x), perm(r0.xa[mt].y), perm(r0.xa[mt].z), perm(r0.xa[mt].w)};
         float c[8];
         raw_codes<NB>(r.u, c);
         const float sc = g_h2f((uint16_t)r.sv);
@@ -992,7 +1008,7 @@ void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t 
                hipStream_t stream)
 {
     const dim3 block(256);
-    if (M > kFusedM && Wr) {
+    if (M > kWsM && Wr) {
         launch_recon_nb<NB>(w, w.N * w.K, w.K, 1, false, Wr, stream);   // N*K: a multiple of 16
         // 128-row tiles halve the LDS and L2 traffic per flop; 64-row tiles when the larger
         // ones would not give every CU two blocks
@@ -1006,9 +1022,11 @@ void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t 
             hipLaunchKernelGGL((gemm_f16_kernel<64, kDepth, kSplitK>),
                                dim3((unsigned)(((M + 63) / 64) * tn)), dim3(256 * kSplitK), 0,
                                stream, X, M, Wr, w.N, w.K, Y);
-    } else if (M > kSkinnyLo && M <= 64 && M * w.K * 2 < 0x7FFFFFF0 &&
+    } else if (M > kSkinnyLo && 64 * w.K * 2 < 0x7FFFFFF0 &&
                (reinterpret_cast<uintptr_t>(w.packed) & (NB == 8 ? 7 : NB == 1 ? 0 : NB == 2 ? 1 : 3)) == 0) {
-        launch_skinny<NB>(X, M, w, Y, stream);
+        // up to 64 rows per launch; more rows (no workspace) in slices of 64
+        for (int64_t m0 = 0; m0 < M; m0 += 64)
+            launch_skinny<NB>(X + m0 * w.K, M - m0 < 64 ? M - m0 : 64, w, Y + m0 * w.N, stream);
     } else if (M <= kSkinnyM && NB != 3 && (w.K * NB) % 32 == 0 &&
                (reinterpret_cast<uintptr_t>(w.packed) & 3) == 0 && M * w.K * 2 < 0x7FFFFFF0 &&
                4 * (w.K * NB / 8) < 0x7FFFFFF0) {
@@ -1058,7 +1076,7 @@ hipError_t launch_recon(const uint8_t *packed, const uint16_t *scale, const void
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    if (M <= kFusedM || N <= 0 || K <= 0 || K > kMaxWsK) return 0;
+    if (M <= kWsM || N <= 0 || K <= 0 || K > kMaxWsK) return 0;
     return ((size_t)N * (size_t)K * 2 + 255) & ~(size_t)255;
 }
 
