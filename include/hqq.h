@@ -177,13 +177,15 @@ hqq_status hqq_dequantize_scales(const uint8_t *scale_q, const void *scale_meta,
  * hqq_dequantize reconstructs from an axis-1 quantized weight (rows N, cols K, same packed /
  * scale / zero / zero_meta layouts); products of binary16 values are accumulated in binary32
  * (in any order) and Y is rounded to binary16. X: binary16 row-major [M, K], 16-byte aligned;
- * Y: binary16 row-major [M, N]. M <= 8 streams the packed weight once per call; larger M runs
- * on the matrix cores.
+ * Y: binary16 row-major [M, N]. Up to M = 64 the packed weight streams once per call (M = 1
+ * on the vector units, 2..64 on the matrix cores); larger M without a workspace streams it
+ * once per 64 rows of X.
  * workspace (optional, device, 16-byte aligned, caller-owned): with M > 64 and at least
  * hqq_gemm_workspace_bytes(M, N, K) bytes, W_r is reconstructed once into it and a plain
- * binary16 GEMM reads it (much faster for large M); NULL keeps the single fused kernel, which
- * reconstructs each weight tile once per 64 rows of X. A non-NULL workspace that is too small
- * is HQQ_ERR_WORKSPACE. Its contents are scratch; calls that share one race. */
+ * binary16 matrix-core GEMM reads it (the faster choice for large M); NULL keeps the
+ * streaming kernels. A non-NULL workspace that is too small is HQQ_ERR_WORKSPACE. Its
+ * contents are scratch; calls that share one race. Packed buffers that are not 4-byte
+ * aligned (8 bytes at 8 bits) take slower fallback kernels. */
 hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *scale,
                     const void *zero, const void *zero_meta, int64_t N, int64_t K, int nbits,
                     int group_size, int zero_bits, void *Y, void *workspace,
