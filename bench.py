@@ -368,6 +368,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-next-rows", action="store_true",
+                    help="only the main step (for a kernel trace of the solver alone)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -498,9 +500,10 @@ def main():
                      "mean_passes": round(mean_passes, 4),
                      "hbm": hbm, "alu": alu},
     }
-    log("bench: 8-bit scales")
-    result["next_rows"] = {"scale8": scale8_row(dev, stream)}
-    if args.workload == 2:
+    if not args.skip_next_rows:
+        log("bench: 8-bit scales")
+        result["next_rows"] = {"scale8": scale8_row(dev, stream)}
+    if args.workload == 2 and not args.skip_next_rows:
         log("bench: axis 0")
         result["next_rows"]["axis0"] = axis0_row(specs, weights, dev, stream, solve_ms)
         log("bench: dequantize")
