@@ -150,12 +150,13 @@ def test_gemm_unaligned_packed_fallback(O, dev, nbits, g, zero_bits):
 
 
 @pytest.mark.parametrize("m,n,k", [(65, 128, 16), (130, 129, 48), (257, 300, 2064),
-                                   (200, 1, 32), (512, 256, 4096), (520, 8200, 272)])
+                                   (200, 1, 32), (512, 256, 4096), (520, 8200, 272),
+                                   (1000, 8200, 80)])
 def test_gemm_workspace_path_shapes(O, dev, m, n, k):
     # the reconstruct-once path: ragged M and N against the 64 x 128 and 128 x 128 tiles (the
-    # last shape has enough tiles for the taller ones), K below one 64-step and with a 16- or
-    # 48-wide tail, a single output column, grids not a multiple of the 8 XCDs; the fused path
-    # on the same inputs must agree with the oracle too
+    # last shape has enough blocks for the taller ones), K below one 64-step and with a 16- or
+    # 48-wide tail, a single output column, grids not a multiple of the 8 XCDs; without the
+    # workspace the same inputs run through the streaming kernels (64-row slices above 64)
     nbits, g, zero_bits = 4, 16, 8
     r = qweight(O, n, k, nbits, g, zero_bits, 5 + m + n + k)
     x16 = synth.half_bits(synth.student_t_weights(m, k, 17 + m)).reshape(-1)
