@@ -118,7 +118,8 @@ __device__ __forceinline__ void recon32(const QW &w, int64_t n, int64_t k0, floa
 }
 
 // ---------------------------------------------------------------------------------------
-// M <= 8: one wave per output row; MB X rows at most (the launch picks 1, 2, 4 or 8).
+// Fallback for M <= 8 (3-bit at M = 1, packed buffers that are not word-aligned): one wave
+// per output row; MB X rows at most (the launch picks 1, 2, 4 or 8).
 // ---------------------------------------------------------------------------------------
 constexpr int kSkinnyM = 8;
 #ifndef HQQ_SKINNY_LO
@@ -229,8 +230,9 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint16_t *__restrict__ 
     }
 }
 
-// M <= 8, bit widths 1, 2, 4, 8 with K*nbits a multiple of 32 and a 4-byte aligned packed
-// buffer: each wave takes R consecutive rows (R > 1 for one X row: the lane's X values are
+// M = 1 (and M <= 8 in the rare shapes the skinny kernel does not take), bit widths 1, 2, 4, 8
+// with K*nbits a multiple of 32 and a 4-byte aligned packed buffer: each wave takes R
+// consecutive rows (R > 1 for one X row: the lane's X values are
 // loaded once and used for every row). A lane takes chunks of 32 codes, 2048 codes apart.
 // Everything is read with buffer loads from wave-uniform bases; an offset past the end of a
 // buffer reads zero, so chunks past K (X = 0: they add nothing) and rows past N need no
@@ -393,7 +395,7 @@ __global__ void __launch_bounds__(256) gemv2_kernel(const uint16_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------------------
-// Larger M: MFMA tiles.
+// Fallback for M > 8 with a packed buffer that is not word-aligned: LDS-staged MFMA tiles.
 // ---------------------------------------------------------------------------------------
 constexpr int BM = 64, BN = 128, BK = 64, LP = BK + 8;   // LDS row pitch (halves)
 
