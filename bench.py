@@ -294,15 +294,17 @@ def dequant_row(specs, outs, dev, stream, reps=5):
 
 def gemm_row(specs, outs, dev, stream, reps=5):
     """The quantized linear layers of the stack (hqq_gemm on the 224 quantized weights the
-    benchmark just wrote). Decode, M = 1: HBM-bound on the packed weights; the 224 calls are
-    captured in a HIP graph (launch gaps would dominate otherwise) and the replay is checked
-    against the eager result. Prefill, M = 512: W_r reconstructed once per call into a
-    workspace, then the binary16 matrix-core GEMM; 2*M*N*K flops."""
+    benchmark just wrote). Decode, M = 1, and small batches, M = 16 and 64 (the weight
+    streams once per call): the 224 calls are captured in a HIP graph (launch gaps would
+    dominate otherwise) and the replay is checked against the eager result; rated against
+    HBM on the bytes of packed weights, scales, zeros, X and Y. Prefill, M = 512: W_r
+    reconstructed once per call into a workspace, then the binary16 matrix-core GEMM;
+    2*M*N*K flops."""
     import torch
     from calibration_free_weight_amd import hqq
     kmax = max(s.cols for s in specs)
     res = {"variant": "quantized linear layers of the stack, Y = X . W_r^T"}
-    for m in (1, 512):
+    for m in (1, 16, 64, 512):
         X = torch.randn(m, kmax, device=dev).to(torch.float16)
         Ys = [torch.empty(m, s.rows, dtype=torch.float16, device=dev) for s in specs]
 
@@ -320,7 +322,7 @@ def gemm_row(specs, outs, dev, stream, reps=5):
         eager = [y.clone() for y in Ys]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         graphed = False
-        if m == 1:
+        if m <= 64:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 run_all()
@@ -349,7 +351,7 @@ def gemm_row(specs, outs, dev, stream, reps=5):
                "bytes": nbytes, "flops": flops,
                "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
-        if m == 1:
+        if m <= 64:
             row.update(bound="hbm", achieved=row["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                        frac=round(row["hbm_gbs"] / HBM_PEAK_GBS, 4))
         else:
