@@ -34,8 +34,9 @@
 //    with its solver state, evaluates it at its candidate zero and takes the stop / accept /
 //    next-zero decision itself. No data moves between lanes and nothing touches memory.
 //  * A group that finishes, or whose decision needs the exact path, leaves its lane for a
-//    staging slot in LDS; the lane takes a ready group from LDS in its place (an exchange
-//    when both exist, so the pool can never block).
+//    staging slot in LDS; the lane takes a ready group from LDS in its place. When both
+//    exist they exchange (in place with LDS atomic swaps for groups up to 64, through a spare
+//    slot for larger ones), so the pool can never block.
 //  * Work that is cheaper across lanes runs in batches of GB groups with KB lanes per group
 //    (EB weights per lane): INIT (a prefetched tile of GB groups: min/max, s, z0, exact
 //    sum x*s; the groups become ready), EXACT (binary64 decisions and shrink updates) and
@@ -115,6 +116,19 @@ HQQ_RED(float, dppf, minf)
 #undef HQQ_RED
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+// LDS atomic swap of 8 bytes (ds_wrxchg_rtn_b64): stores v, returns the old contents.
+__device__ __forceinline__ uint64_t xchg_l(uint64_t *p, uint64_t v)
+{
+    return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ uint64_t pack2(float a, float b)
+{
+    return (uint64_t)__float_as_uint(a) | (uint64_t)__float_as_uint(b) << 32;
+}
+__device__ __forceinline__ uint64_t pack2(float a, uint32_t b) { return (uint64_t)__float_as_uint(a) | (uint64_t)b << 32; }
+__device__ __forceinline__ uint64_t pack2(uint32_t a, uint32_t b) { return (uint64_t)a | (uint64_t)b << 32; }
+__device__ __forceinline__ float lo_f(uint64_t v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ float hi_f(uint64_t v) { return __uint_as_float((uint32_t)(v >> 32)); }
 __device__ __forceinline__ int lanes_below(uint64_t mask)
 {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
@@ -183,16 +197,24 @@ struct Cfg {
     static constexpr int RC = GB >= 32 ? 128 : 64;  // ring capacity
     static constexpr int LDS_WAVE = 163840 / (4 * WAVES) / 1280 * 1280;
     static constexpr int LDS_FREE = LDS_WAVE - 4 * RC - (NBITS == 3 ? 64 * EB : 0) - 128;
-    // the spare slot and one more column (for an odd stride) come out of the budget first
-    static constexpr int NS_FIT = (LDS_FREE - 2 * (2 * G + 48)) / (2 * G + 48);
+    // How groups move between lanes and slots. Groups up to 64 swap in place with LDS atomic
+    // exchanges (half the swaps, measured 10-13 % faster at g16-g64); larger groups move with
+    // 16-byte stores and loads through free slots and a spare slot (the exchanges of 256-byte
+    // groups measured 1.5-3 % slower at g128).
+    static constexpr bool XCHG = G <= 64;
+    static_assert(!XCHG || KP == 1, "in-place swaps move one lane per group");
+    // one more column of weights (for an odd stride) comes out of the budget first, and with
+    // the spare slot two whole slots
+    static constexpr int NS_FIT = (LDS_FREE - (XCHG ? 2 * G : 2 * (2 * G + 48))) / (2 * G + 48);
 #ifdef HQQ_STRESS_SLOTS
-    // stress build for the tests: a pool of one batch plus a few slots, so that lanes must
-    // often exchange their group with a ready one
+    // stress build for the tests: a pool of one batch plus a few slots, so that free slots
+    // are scarce and holders often swap in place or wait
     static constexpr int NS = GB + HQQ_STRESS_SLOTS;
 #else
     static constexpr int NS = NS_FIT < 3 * GB ? NS_FIT : 3 * GB;   // staging slots
 #endif
-    static constexpr int CS = (NS + 1) | 1;         // chunk stride: slots and spare, odd
+    static constexpr int NSP = XCHG ? NS : NS + 1;  // slots including the spare
+    static constexpr int CS = NSP | 1;              // chunk stride: odd, at least NSP
     static_assert(NS >= GB + 4 && NS <= RC, "staging slots");
     static constexpr float QMAX = (float)((1 << NBITS) - 1);
     // A binary32 code can disagree with the exact one only if |u - rne(u)| >= kThr.
@@ -303,14 +325,14 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     using C = Cfg<NBITS, G>;
     constexpr int KP = C::KP, WP = C::WP, EB = C::EB, KB = C::KB, GB = C::GB, WB = C::WB;
     constexpr int NS = C::NS, RM = C::RC - 1;
-    constexpr int kSpare = NS;                   // the spare slot (in no ring)
     static_assert(NS <= 255, "slot indices are bytes");
+    constexpr int kSpare = NS;                   // the spare slot (in no ring), g > 64 only
 
-    // Staging slots and the spare: weights and per-group state (one array per field).
+    // Staging slots (and the spare): weights and per-group state (one array per field).
     __shared__ __attribute__((aligned(16))) uint16_t xs[C::CS * G];
-    __shared__ SlotA st_a[NS + 1];
-    __shared__ SlotB st_b[NS + 1];
-    __shared__ SlotC st_c[NS + 1];
+    __shared__ SlotA st_a[C::NSP];
+    __shared__ SlotB st_b[C::NSP];
+    __shared__ SlotC st_c[C::NSP];
     __shared__ uint8_t rings[4 * C::RC];   // slot rings: ready, finished, exact-pending, free
     uint8_t *const ring_rdy = rings, *const ring_fin = rings + C::RC,
                    *const ring_exq = rings + 2 * C::RC, *const ring_free = rings + 3 * C::RC;
@@ -454,6 +476,18 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     auto cur_state = [&]() -> GroupState {
         return GroupState{SlotA{g_s, g_z, g_zb, g_Db}, SlotB{g_beta, g_mnmx, g_gidx, g_meta},
                           SlotC{g_Sb, g_X}};
+    };
+    // Swaps the state in slot j with n (LDS atomic swaps, 8 bytes each); returns the old state.
+    auto xchg_state = [&](int j, const GroupState &n) -> GroupState {
+        uint64_t *pa = reinterpret_cast<uint64_t *>(&st_a[j]);
+        uint64_t *pb = reinterpret_cast<uint64_t *>(&st_b[j]);
+        uint64_t *pc = reinterpret_cast<uint64_t *>(&st_c[j]);
+        const uint64_t a0 = xchg_l(pa, pack2(n.a.s, n.a.z)), a1 = xchg_l(pa + 1, pack2(n.a.zb, n.a.Db));
+        const uint64_t b0 = xchg_l(pb, pack2(n.b.beta, n.b.mnmx)), b1 = xchg_l(pb + 1, pack2(n.b.gidx, n.b.meta));
+        const uint64_t c0 = xchg_l(pc, __double_as_longlong(n.c.Sb)), c1 = xchg_l(pc + 1, __double_as_longlong(n.c.X));
+        return GroupState{SlotA{lo_f(a0), hi_f(a0), lo_f(a1), hi_f(a1)},
+                          SlotB{lo_f(b0), (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32)},
+                          SlotC{__longlong_as_double(c0), __longlong_as_double(c1)}};
     };
     auto set_state = [&](const GroupState &n) {
         g_s = n.a.s;
@@ -662,82 +696,146 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             const uint32_t n_empty = (uint32_t)__builtin_popcountll(m_empty);
 
             // A tile comes in first when the ready groups cannot fill the lanes about to need
-            // one and the slots stay enough for every holder: one swap then serves them all.
-            if (pf_ok && rdy_n < n_empty + n_hold && fre_n >= GB + n_hold) break;   // INIT
+            // one and the free slots take the tile and every holder that needs a free slot
+            // (with in-place swaps, those the ready groups and the tile's cannot take): one
+            // swap then serves them all.
+            const uint32_t partners = C::XCHG ? rdy_n + GB : 0u;
+            if (pf_ok && rdy_n < n_empty + n_hold &&
+                fre_n >= GB + (n_hold > partners ? n_hold - partners : 0u))
+                break;   // INIT
 
             if ((n_hold > 0 && (rdy_n > 0 || fre_n > 0)) || (n_empty > 0 && rdy_n > 0)) {
                 // ================= SWAP: groups leave lanes for slots and enter from slots ====
-                // Holders store their group in a free slot; lanes left without a group load a
-                // ready one. When no slot is free, one holder exchanges its group with a ready
-                // one through the spare slot: the ready group is copied there, the holder's
-                // group takes its slot, and the holder loads from the spare like any other
-                // lane (so the weight registers have a single load site).
-                const uint32_t n_out = n_hold < fre_n ? n_hold : fre_n;
-                const uint32_t n_x = (n_out < n_hold && fre_n == 0 && rdy_n > 0) ? 1u : 0u;
-                const uint32_t rk_h = group_rank(m_hold, pbase);
-                const bool out_l = holder && rk_h < n_out;
-                const bool exch_l = n_x > 0 && holder && rk_h == n_out;
-                const bool no_group = status == kEmpty || out_l;
-                const uint64_t m_ng = __ballot(no_group && lead);
-                const uint32_t n_ng = (uint32_t)__builtin_popcountll(m_ng);
-                const uint32_t n_in = n_ng < rdy_n - n_x ? n_ng : rdy_n - n_x;
-                const uint32_t rk_n = group_rank(m_ng, pbase);
-                const bool in_l = no_group && rk_n < n_in;
-                const bool st = out_l || exch_l, ld = in_l || exch_l;
-                int jo = 0, ji = 0;
-                if (out_l) jo = ring_free[(fre_h + rk_h) & RM];
-                if (exch_l) jo = ring_rdy[rdy_h & RM];
-                if (in_l) ji = ring_rdy[(rdy_h + n_x + rk_n) & RM];
-                if (exch_l) ji = kSpare;
-                if (n_x > 0 && exch_l) {             // the ready group moves to the spare slot
-#pragma unroll
-                    for (int c = 0; c < WP / 4; ++c) {
-                        const int off = part * (WP / 4) + c;
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(jo, off));
-                        *reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(kSpare, off)) = v;
+                // Every lane moves through one slot, so the weight registers have a single load
+                // site (no copies at joins).
+                if constexpr (C::XCHG) {
+                    // In place: a holder swaps its group with a ready one through the ready
+                    // group's slot (LDS atomic exchanges), so the exchange needs no free slot.
+                    // Holders left without a ready group swap into free slots; lanes without a
+                    // group swap the remaining ready groups out of theirs.
+                    const uint32_t n_xc = n_hold < rdy_n ? n_hold : rdy_n;
+                    const uint32_t n_left = n_hold - n_xc;
+                    const uint32_t n_out = n_left < fre_n ? n_left : fre_n;
+                    const uint32_t n_in = n_empty < rdy_n - n_xc ? n_empty : rdy_n - n_xc;
+                    const uint32_t rk_h = group_rank(m_hold, pbase);
+                    const uint32_t rk_e = group_rank(m_empty, pbase);
+                    const bool xc_l = holder && rk_h < n_xc;
+                    const bool out_l = holder && rk_h >= n_xc && rk_h < n_xc + n_out;
+                    const bool in_l = status == kEmpty && rk_e < n_in;
+                    const bool st = xc_l || out_l, ld = xc_l || in_l;
+                    int j = 0;
+                    if (xc_l) j = ring_rdy[(rdy_h + rk_h) & RM];
+                    if (out_l) j = ring_free[(fre_h + rk_h - n_xc) & RM];
+                    if (in_l) j = ring_rdy[(rdy_h + n_xc + rk_e) & RM];
+                    if (st || ld) {
+                        // Every moving lane exchanges its registers with slot j (LDS atomic swaps):
+                        // a lane that only loads writes don't-care values into a slot that becomes
+                        // free, a lane that only stores reads don't-care values and becomes empty.
+    #pragma unroll
+                        for (int c = 0; c < WP / 4; ++c) {
+                            uint64_t *p = reinterpret_cast<uint64_t *>(xs + chunk_at<C::CS>(j, part * (WP / 4) + c));
+                            const uint64_t lo = xchg_l(p, (uint64_t)xr[4 * c] | (uint64_t)xr[4 * c + 1] << 32);
+                            const uint64_t hi = xchg_l(p + 1, (uint64_t)xr[4 * c + 2] | (uint64_t)xr[4 * c + 3] << 32);
+                            xr[4 * c] = (uint32_t)lo;
+                            xr[4 * c + 1] = (uint32_t)(lo >> 32);
+                            xr[4 * c + 2] = (uint32_t)hi;
+                            xr[4 * c + 3] = (uint32_t)(hi >> 32);
+                        }
+                        set_state(xchg_state(j, cur_state()));
                     }
-                    const GroupState ns = load_state(jo);
-                    if (lead) put_state(kSpare, ns);
-                }
-                if (st) {
-#pragma unroll
-                    for (int c = 0; c < WP / 4; ++c)
-                        *reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(jo, part * (WP / 4) + c)) =
-                            u32x4{xr[4 * c], xr[4 * c + 1], xr[4 * c + 2], xr[4 * c + 3]};
-                    if (lead) put_state(jo, cur_state());
-                }
-                if (ld) {
-#pragma unroll
-                    for (int c = 0; c < WP / 4; ++c) {
-                        const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(ji, part * (WP / 4) + c));
-                        xr[4 * c] = v.x;
-                        xr[4 * c + 1] = v.y;
-                        xr[4 * c + 2] = v.z;
-                        xr[4 * c + 3] = v.w;
+                    // rings: stored groups go to finished / exact-pending; the slots of groups
+                    // loaded into empty lanes become free
+                    const bool to_fin = st && status == kHoldFin;
+                    const uint64_t m_f = __ballot(to_fin && lead);
+                    const uint64_t m_x = __ballot(st && !to_fin && lead);
+                    const uint64_t m_fr = __ballot(in_l && lead);
+                    if (st && lead) {
+                        if (to_fin) ring_fin[(fin_h + fin_n + lanes_below(m_f)) & RM] = (uint8_t)j;
+                        else ring_exq[(exq_h + exq_n + lanes_below(m_x)) & RM] = (uint8_t)j;
                     }
-                    set_state(load_state(ji));
+                    rdy_h = (rdy_h + n_xc + n_in) & RM;
+                    rdy_n -= n_xc + n_in;
+                    fre_h = (fre_h + n_out) & RM;
+                    fre_n -= n_out;
+                    if (in_l && lead) ring_free[(fre_h + fre_n + lanes_below(m_fr)) & RM] = (uint8_t)j;
+                    fre_n += (uint32_t)__builtin_popcountll(m_fr);
+                    fin_n += (uint32_t)__builtin_popcountll(m_f);
+                    exq_n += (uint32_t)__builtin_popcountll(m_x);
+                    if (ld) status = kActive;
+                    else if (out_l) status = kEmpty;
+                } else {
+                    // Through free slots: holders store their group in a free slot; lanes left
+                    // without a group load a ready one. When no slot is free, one holder
+                    // exchanges its group with a ready one through the spare slot: the ready
+                    // group is copied there, the holder's group takes its slot, and the holder
+                    // loads from the spare like any other lane.
+                    const uint32_t n_out = n_hold < fre_n ? n_hold : fre_n;
+                    const uint32_t n_x = (n_out < n_hold && fre_n == 0 && rdy_n > 0) ? 1u : 0u;
+                    const uint32_t rk_h = group_rank(m_hold, pbase);
+                    const bool out_l = holder && rk_h < n_out;
+                    const bool exch_l = n_x > 0 && holder && rk_h == n_out;
+                    const bool no_group = status == kEmpty || out_l;
+                    const uint64_t m_ng = __ballot(no_group && lead);
+                    const uint32_t n_ng = (uint32_t)__builtin_popcountll(m_ng);
+                    const uint32_t n_in = n_ng < rdy_n - n_x ? n_ng : rdy_n - n_x;
+                    const uint32_t rk_n = group_rank(m_ng, pbase);
+                    const bool in_l = no_group && rk_n < n_in;
+                    const bool st = out_l || exch_l, ld = in_l || exch_l;
+                    int jo = 0, ji = 0;
+                    if (out_l) jo = ring_free[(fre_h + rk_h) & RM];
+                    if (exch_l) jo = ring_rdy[rdy_h & RM];
+                    if (in_l) ji = ring_rdy[(rdy_h + n_x + rk_n) & RM];
+                    if (exch_l) ji = kSpare;
+                    if (n_x > 0 && exch_l) {             // the ready group moves to the spare slot
+    #pragma unroll
+                        for (int c = 0; c < WP / 4; ++c) {
+                            const int off = part * (WP / 4) + c;
+                            const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(jo, off));
+                            *reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(kSpare, off)) = v;
+                        }
+                        const GroupState ns = load_state(jo);
+                        if (lead) put_state(kSpare, ns);
+                    }
+                    if (st) {
+    #pragma unroll
+                        for (int c = 0; c < WP / 4; ++c)
+                            *reinterpret_cast<u32x4 *>(xs + chunk_at<C::CS>(jo, part * (WP / 4) + c)) =
+                                u32x4{xr[4 * c], xr[4 * c + 1], xr[4 * c + 2], xr[4 * c + 3]};
+                        if (lead) put_state(jo, cur_state());
+                    }
+                    if (ld) {
+    #pragma unroll
+                        for (int c = 0; c < WP / 4; ++c) {
+                            const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(ji, part * (WP / 4) + c));
+                            xr[4 * c] = v.x;
+                            xr[4 * c + 1] = v.y;
+                            xr[4 * c + 2] = v.z;
+                            xr[4 * c + 3] = v.w;
+                        }
+                        set_state(load_state(ji));
+                    }
+                    // rings: stored groups go to finished / exact-pending; the slots of loaded
+                    // groups become free
+                    const bool stored = st;
+                    const bool to_fin = stored && status == kHoldFin;
+                    const uint64_t m_f = __ballot(to_fin && lead);
+                    const uint64_t m_x = __ballot(stored && !to_fin && lead);
+                    const uint64_t m_fr = __ballot(in_l && lead);
+                    if (stored && lead) {
+                        if (to_fin) ring_fin[(fin_h + fin_n + lanes_below(m_f)) & RM] = (uint8_t)jo;
+                        else ring_exq[(exq_h + exq_n + lanes_below(m_x)) & RM] = (uint8_t)jo;
+                    }
+                    rdy_h = (rdy_h + n_x + n_in) & RM;
+                    rdy_n -= n_x + n_in;
+                    fre_h = (fre_h + n_out) & RM;
+                    fre_n -= n_out;
+                    if (in_l && lead) ring_free[(fre_h + fre_n + lanes_below(m_fr)) & RM] = (uint8_t)ji;
+                    fre_n += (uint32_t)__builtin_popcountll(m_fr);
+                    fin_n += (uint32_t)__builtin_popcountll(m_f);
+                    exq_n += (uint32_t)__builtin_popcountll(m_x);
+                    if (ld) status = kActive;
+                    else if (out_l) status = kEmpty;
                 }
-                // rings: stored groups go to finished / exact-pending; the slots of loaded
-                // groups become free
-                const bool stored = st;
-                const bool to_fin = stored && status == kHoldFin;
-                const uint64_t m_f = __ballot(to_fin && lead);
-                const uint64_t m_x = __ballot(stored && !to_fin && lead);
-                const uint64_t m_fr = __ballot(in_l && lead);
-                if (stored && lead) {
-                    if (to_fin) ring_fin[(fin_h + fin_n + lanes_below(m_f)) & RM] = (uint8_t)jo;
-                    else ring_exq[(exq_h + exq_n + lanes_below(m_x)) & RM] = (uint8_t)jo;
-                }
-                rdy_h = (rdy_h + n_x + n_in) & RM;
-                rdy_n -= n_x + n_in;
-                fre_h = (fre_h + n_out) & RM;
-                fre_n -= n_out;
-                if (in_l && lead) ring_free[(fre_h + fre_n + lanes_below(m_fr)) & RM] = (uint8_t)ji;
-                fre_n += (uint32_t)__builtin_popcountll(m_fr);
-                fin_n += (uint32_t)__builtin_popcountll(m_f);
-                exq_n += (uint32_t)__builtin_popcountll(m_x);
-                if (ld) status = kActive;
-                else if (out_l) status = kEmpty;
                 continue;
             }
 
