@@ -193,7 +193,8 @@ struct Cfg {
     // bytes per wave let 12 waves share a compute unit, 13,032 only 11), holds each slot's
     // weights and 48 bytes of state, the rings and the 3-bit code stage; at most three
     // batches of slots.
-    static constexpr int WAVES = G <= 16 ? 4 : (G <= 128 ? 3 : 2);
+    // (3-bit g32 stays at three: its code stage leaves fewer slots than four waves need.)
+    static constexpr int WAVES = (G <= 16 || (G == 32 && NBITS != 3)) ? 4 : (G <= 128 ? 3 : 2);
     static constexpr int RC = GB >= 32 ? 128 : 64;  // ring capacity
     static constexpr int LDS_WAVE = 163840 / (4 * WAVES) / 1280 * 1280;
     static constexpr int LDS_FREE = LDS_WAVE - 4 * RC - (NBITS == 3 ? 64 * EB : 0) - 128;
