@@ -657,6 +657,25 @@ hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *sc
     return HQQ_OK;
 }
 
+hqq_status hqq_gemm_f16(const void *X, int64_t M, const void *Wr, int64_t N, int64_t K, void *Y,
+                        void *stream)
+{
+    if (M < 0 || N < 0 || K < 0) return fail(HQQ_ERR_ARG, "M, N and K must be >= 0");
+    if (M == 0 || N == 0) return HQQ_OK;
+    if (!hqq::gemm_f16_fits(N, K))
+        return fail(HQQ_ERR_ARG, "K must be a positive multiple of 8 and at most 2^22");
+    if (M > (int64_t(1) << 40) / K) return fail(HQQ_ERR_ARG, "M*K too large");
+    if (!X || !Wr || !Y) return fail(HQQ_ERR_ARG, "X, Wr and Y must be non-null");
+    if (!aligned(X, 16) || !aligned(Wr, 16)) return fail(HQQ_ERR_ARG, "X and Wr must be 16-byte aligned");
+    if (!aligned(Y, 2)) return fail(HQQ_ERR_ARG, "Y must be 2-byte aligned");
+    hipError_t e = hqq::launch_gemm_f16(static_cast<const uint16_t *>(X), M,
+                                        static_cast<const uint16_t *>(Wr), N, K,
+                                        static_cast<uint16_t *>(Y), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "gemm_f16 launch");
+    g_last_error.clear();
+    return HQQ_OK;
+}
+
 hqq_status hqq_pack(const uint8_t *codes, int64_t n_codes, int nbits, void *packed, void *stream)
 {
     if (!valid_bits(nbits)) return fail(HQQ_ERR_ARG, "nbits must be 1, 2, 3, 4 or 8");

@@ -1005,6 +1005,24 @@ void launch_gemv2(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStr
     else hipLaunchKernelGGL((gemv2_kernel<NB, 8, 1, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
 }
 
+// Y = X . Wr^T for a binary16 Wr [N, K] (K a multiple of 8, at most kMaxWsK).
+void launch_f16(const uint16_t *X, int64_t M, const uint16_t *Wr, int64_t N, int64_t K,
+                uint16_t *Y, hipStream_t stream)
+{
+    // 128-row tiles halve the LDS and L2 traffic per flop; 64-row tiles when the larger ones
+    // would not give every CU two blocks
+    const int64_t tn = (N + BN - 1) / BN;
+    const bool tall = kBM16 == 128 || (kBM16 == 0 && ((M + 127) / 128) * tn >= 512);
+    if (tall)
+        hipLaunchKernelGGL((gemm_f16_kernel<128, kDepth, kSplitK>),
+                           dim3((unsigned)(((M + 127) / 128) * tn)), dim3(256 * kSplitK), 0,
+                           stream, X, M, Wr, N, K, Y);
+    else
+        hipLaunchKernelGGL((gemm_f16_kernel<64, kDepth, kSplitK>),
+                           dim3((unsigned)(((M + 63) / 64) * tn)), dim3(256 * kSplitK), 0,
+                           stream, X, M, Wr, N, K, Y);
+}
+
 template <int NB>
 void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t *Wr,
                hipStream_t stream)
@@ -1012,18 +1030,7 @@ void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t 
     const dim3 block(256);
     if (M > kWsM && Wr) {
         launch_recon_nb<NB>(w, w.N * w.K, w.K, 1, false, Wr, stream);   // N*K: a multiple of 16
-        // 128-row tiles halve the LDS and L2 traffic per flop; 64-row tiles when the larger
-        // ones would not give every CU two blocks
-        const int64_t tn = (w.N + BN - 1) / BN;
-        const bool tall = kBM16 == 128 || (kBM16 == 0 && ((M + 127) / 128) * tn >= 512);
-        if (tall)
-            hipLaunchKernelGGL((gemm_f16_kernel<128, kDepth, kSplitK>),
-                               dim3((unsigned)(((M + 127) / 128) * tn)), dim3(256 * kSplitK), 0,
-                               stream, X, M, Wr, w.N, w.K, Y);
-        else
-            hipLaunchKernelGGL((gemm_f16_kernel<64, kDepth, kSplitK>),
-                               dim3((unsigned)(((M + 63) / 64) * tn)), dim3(256 * kSplitK), 0,
-                               stream, X, M, Wr, w.N, w.K, Y);
+        launch_f16(X, M, Wr, w.N, w.K, Y, stream);
     } else if (M > kSkinnyLo && 64 * w.K * 2 < 0x7FFFFFF0 &&
                (reinterpret_cast<uintptr_t>(w.packed) & (NB == 8 ? 7 : NB == 1 ? 0 : NB == 2 ? 1 : 3)) == 0) {
         // up to 64 rows per launch; more rows (no workspace) in slices of 64
@@ -1080,6 +1087,15 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M <= kWsM || N <= 0 || K <= 0 || K > kMaxWsK) return 0;
     return ((size_t)N * (size_t)K * 2 + 255) & ~(size_t)255;
+}
+
+bool gemm_f16_fits(int64_t N, int64_t K) { return N > 0 && K > 0 && K % 8 == 0 && K <= kMaxWsK; }
+
+hipError_t launch_gemm_f16(const uint16_t *X, int64_t M, const uint16_t *Wr, int64_t N, int64_t K,
+                           uint16_t *Y, hipStream_t stream)
+{
+    launch_f16(X, M, Wr, N, K, Y, stream);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint16_t *X, int64_t M, const uint8_t *packed, const uint16_t *scale,

@@ -80,6 +80,10 @@ bool recon_fits(const void *packed, int nbits, int64_t cols, int axis, const voi
 hipError_t launch_recon(const uint8_t *packed, const uint16_t *scale, const void *zero,
                         const uint16_t *zero_meta, int64_t rows, int64_t cols, int nbits, int g,
                         int zero_bits, int axis, uint16_t *out, hipStream_t stream);
+// Y = X . Wr^T with a binary16 Wr [N, K] on the matrix cores; gemm_f16_fits(N, K) must hold
+bool gemm_f16_fits(int64_t N, int64_t K);
+hipError_t launch_gemm_f16(const uint16_t *X, int64_t M, const uint16_t *Wr, int64_t N, int64_t K,
+                           uint16_t *Y, hipStream_t stream);
 // Wr: binary16 [N, K] workspace of gemm_workspace_bytes(M, N, K) bytes, or nullptr
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint16_t *X, int64_t M, const uint8_t *packed, const uint16_t *scale,

@@ -19,7 +19,7 @@ HQQ_OK, HQQ_ERR_ARG, HQQ_ERR_UNSUPPORTED, HQQ_ERR_WORKSPACE, HQQ_ERR_DEVICE = ra
 EXPORTS = ("hqq_packed_bytes", "hqq_workspace_bytes", "hqq_quantize", "hqq_quantize_batch",
            "hqq_solve_batch", "hqq_requant_batch", "hqq_quantize_streamed",
            "hqq_streamed_workspace_bytes", "hqq_dequantize", "hqq_gemm",
-           "hqq_gemm_workspace_bytes", "hqq_requant_scales",
+           "hqq_gemm_workspace_bytes", "hqq_gemm_f16", "hqq_requant_scales",
            "hqq_dequantize_scales", "hqq_pack", "hqq_unpack", "hqq_status_string",
            "hqq_last_error")
 
@@ -72,6 +72,8 @@ def lib():
                                C.c_size_t, vp]
         L.hqq_gemm_workspace_bytes.restype = C.c_size_t
         L.hqq_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.hqq_gemm_f16.restype = i32
+        L.hqq_gemm_f16.argtypes = [vp, i64, vp, i64, i64, vp, vp]
         L.hqq_requant_scales.restype = i32
         L.hqq_requant_scales.argtypes = [vp, i64, i32, vp, vp, vp]
         L.hqq_dequantize_scales.restype = i32
@@ -201,6 +203,11 @@ def hqq_gemm(X, packed, scale, zero, zero_meta, N, K, nbits, group_size, zero_bi
 
 def hqq_gemm_workspace_bytes(M, N, K) -> int:
     return int(lib().hqq_gemm_workspace_bytes(M, N, K))
+
+
+def hqq_gemm_f16(X, Wr, N, K, Y, stream=None) -> None:
+    """Y[M, N] = X[M, K] . Wr^T for a binary16 weight Wr [N, K] (as hqq_dequantize writes it)."""
+    _check(lib().hqq_gemm_f16(_p(X), X.shape[0], _p(Wr), N, K, _p(Y), _stream(stream)))
 
 
 def hqq_requant_scales(scale, n, scale_group, scale_q, scale_meta, stream=None) -> None:

@@ -195,6 +195,17 @@ hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *sc
  * else 0 (no workspace is used). */
 size_t hqq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/* The same layer in two steps [SK "HQQLinear layer": the layer computes with the dequantized
+ * weight]: given Wr, the binary16 weight [N, K] that hqq_dequantize wrote, Y[M, N] = X[M, K] .
+ * Wr^T with binary32 sums (any order) rounded to binary16, on the matrix-core kernel of
+ * hqq_gemm's reconstruct-once path (for the same Wr, the two give identical Y). For callers
+ * that keep Wr resident and multiply it many times, so the reconstruction is paid once.
+ * X and Wr: binary16 row-major, 16-byte aligned; Y: binary16 row-major [M, N],
+ * 2-byte aligned. K: a positive multiple of 8, at most 2^22, else HQQ_ERR_ARG. M = 0 or N = 0
+ * does nothing. Nothing is allocated; the call only enqueues on `stream`. */
+hqq_status hqq_gemm_f16(const void *X, int64_t M, const void *Wr, int64_t N, int64_t K, void *Y,
+                        void *stream);
+
 /* Pack n_codes uint8 codes (each < 2^nbits) into the packed layout above; `packed` must be
  * 16-byte aligned and hold hqq_packed_bytes(n_codes, nbits) bytes. Codes >= 2^nbits are
  * masked to their low nbits bits. */

@@ -21,7 +21,7 @@ def H():
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "hqq.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(hqq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(hqq_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(H):
@@ -156,6 +156,28 @@ def test_streamed_entry_points_validate(H):
         H.HQQ_ERR_ARG
     empty = (H.hqq_job * 1)(_job(H, rows=0))
     assert L.hqq_quantize_streamed(empty, 1, None, 0, None, 0, None, None) == H.HQQ_OK
+
+
+def test_gemm_f16_validates(H):
+    """hqq_gemm_f16 rejects bad sizes and alignments on the host (fake device addresses: a
+    rejected call reaches no HIP call) and treats empty products as done."""
+    L = H.lib()
+    X, W, Y = (C.c_void_p(a) for a in (0x1000, 0x2000, 0x3000))
+    ok, arg = H.HQQ_OK, H.HQQ_ERR_ARG
+    g = lambda x, m, w, n, k, y: L.hqq_gemm_f16(x, m, w, n, k, y, None)
+    assert g(None, 0, None, 64, 128, None) == ok                      # M = 0
+    assert g(None, 4, None, 0, 128, None) == ok                       # N = 0
+    assert g(X, -1, W, 64, 128, Y) == arg
+    assert g(X, 4, W, 64, -8, Y) == arg
+    for k in (0, 4, 100, (1 << 22) + 8):                              # K % 8, 0 < K <= 2^22
+        assert g(X, 4, W, 64, k, Y) == arg, k
+    assert g(None, 4, W, 64, 128, Y) == arg
+    assert g(X, 4, None, 64, 128, Y) == arg
+    assert g(X, 4, W, 64, 128, None) == arg
+    assert g(C.c_void_p(0x1008), 4, W, 64, 128, Y) == arg              # X 16-byte aligned
+    assert g(X, 4, C.c_void_p(0x2008), 64, 128, Y) == arg              # Wr 16-byte aligned
+    assert g(X, 4, W, 64, 128, C.c_void_p(0x3001)) == arg              # Y 2-byte aligned
+    assert g(X, 1 << 30, W, 64, 4096, Y) == arg                        # M*K too large
 
 
 def test_gemm_validates(H):

@@ -233,3 +233,47 @@ def test_reconstruction_ties_bit_exact(O, dev):
                      workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(Y.cpu().numpy(), ref[:, :m].T), f"m={m} workspace={use_ws}"
+
+
+def run_f16(x16, w16, m, n, k, dev):
+    X = to_dev(x16, np.int16, dev).view(m, k)
+    W = to_dev(w16, np.int16, dev).view(n, k)
+    Y = torch.full((m, n), float("nan"), dtype=torch.float16, device=dev)
+    hqq.hqq_gemm_f16(X, W, n, k, Y)
+    torch.cuda.synchronize()
+    return u16(Y).view(np.float16).astype(np.float64).reshape(m, n)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 8), (3, 15, 24), (65, 200, 1032), (129, 130, 8),
+                                   (300, 257, 4104)])
+def test_gemm_f16_matches_binary64_product(dev, m, n, k):
+    # hqq_gemm_f16 on a plain binary16 weight: M = 1, one output column, K of one 8-wide
+    # chunk and with 8- and 24-wide tails past the 64-wide steps, ragged M and N against the
+    # tiles; the reference is the binary64 product (a library matmul), the tolerance the
+    # binary32 summation plus the final rounding, as for hqq_gemm
+    x16 = synth.half_bits(synth.student_t_weights(m, k, 31 + m)).reshape(-1)
+    x16 = (x16.view(np.float16).astype(np.float32) * 40).astype(np.float16).view(np.uint16)
+    w16 = synth.half_bits(synth.student_t_weights(n, k, 37 + n)).reshape(-1)
+    print(f"gemm_f16 m={m} n={n} k={k}", flush=True)
+    y = run_f16(x16, w16, m, n, k, dev)
+    x = x16.view(np.float16).astype(np.float64).reshape(m, k)
+    w = w16.view(np.float16).astype(np.float64).reshape(n, k)
+    ref = x @ w.T
+    tol = (k + 1) * 2.0 ** -24 * (np.abs(x) @ np.abs(w).T) + np.maximum(2.0 ** -11 * np.abs(ref), 2.0 ** -25)
+    assert not np.isnan(y).any(), "unwritten outputs"
+    assert np.all(np.abs(y - ref) <= tol * (1 + 1e-9)), f"max err/tol {np.max(np.abs(y - ref) / tol):.3f}"
+
+
+@pytest.mark.parametrize("m,n,k", [(130, 129, 48), (520, 8200, 272)])
+def test_gemm_f16_equals_workspace_path(O, dev, m, n, k):
+    # the two-step layer (the oracle's W_r, then hqq_gemm_f16) and hqq_gemm's reconstruct-once
+    # path run one kernel on the same W_r, so Y is identical
+    nbits, g, zero_bits = 4, 16, 8
+    r = qweight(O, n, k, nbits, g, zero_bits, 41 + m + n + k)
+    x16 = synth.half_bits(synth.student_t_weights(m, k, 43 + m)).reshape(-1)
+    wr = O.dequantize(r["codes"], r["scale"], r["zero"], r["zero_meta"], g, zero_bits)
+    print(f"gemm_f16 vs workspace m={m} n={n} k={k}", flush=True)
+    y2 = run_f16(x16, np.ascontiguousarray(wr).view(np.uint16).reshape(-1), m, n, k, dev)
+    y1 = run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev, workspace=True)
+    assert not np.isnan(y2).any()
+    assert np.array_equal(y1, y2)
