@@ -292,7 +292,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                              nr, 0x00020000);
 }
 
-template <int NB, int MB, int R, int ZB>
+template <int NB, int MB, int R, int ZB, int ITV = 0>
 __global__ void __launch_bounds__(256) gemv2_kernel(const uint16_t *__restrict__ X, int M, QW w,
                                                     uint16_t *__restrict__ Y)
 {
@@ -318,7 +318,7 @@ __global__ void __launch_bounds__(256) gemv2_kernel(const uint16_t *__restrict__
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[m][r] = 0.0f;
 
-    constexpr int IT = MB >= 4 ? 1 : 2;          // chunks per lane in flight
+    constexpr int IT = ITV ? ITV : (MB >= 4 ? 1 : 2);   // chunks per lane in flight
     const int64_t steps = (w.K + 2047) >> 11;    // chunks of the row per lane (some past K)
     for (int64_t j0 = 0; j0 < steps; j0 += IT) {
         uint32_t wd[IT][R][NB];
@@ -996,7 +996,12 @@ void launch_gemv2(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStr
     if (M == 1) {
         constexpr int R = kGemvRows;
         const dim3 grid((unsigned)((w.N + 4 * R - 1) / (4 * R)));
-        hipLaunchKernelGGL((gemv2_kernel<NB, 1, R, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
+        // rows of more than two chunks per lane keep three in flight (the 11008-wide rows of
+        // an MLP down projection then take two load rounds instead of three; six were slower)
+        if (((w.K + 2047) >> 11) > 2)
+            hipLaunchKernelGGL((gemv2_kernel<NB, 1, R, ZB, 3>), grid, block, 0, stream, X, (int)M, w, Y);
+        else
+            hipLaunchKernelGGL((gemv2_kernel<NB, 1, R, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
         return;
     }
     const dim3 grid((unsigned)((w.N + 3) / 4));

@@ -88,10 +88,12 @@ def test_gemm_matches_oracle(O, dev, nbits, g, zero_bits, m):
 def test_gemm_decode_ragged(O, dev, nbits, g, zero_bits):
     # the decode kernels on ragged shapes: odd N (a wave's second row missing), one row,
     # K below one chunk of 32 codes per lane, between chunks, and past one 2048-code sweep
-    # (with g = 16, K % 32 == 16: a lane's last chunk ends half past the row);
-    # packed buffers offset by 4 bytes (still word-aligned) and by 1 byte (the fallback)
+    # (with g = 16, K % 32 == 16: a lane's last chunk ends half past the row), past two
+    # sweeps (M = 1: three chunks per lane in flight) and past four (two rounds of three, the
+    # second partly past the row); packed buffers offset by 4 bytes (still word-aligned) and
+    # by 1 byte (the fallback)
     for m in (1, 2, 5, 8):
-        for n, k in ((1, g), (3, 3 * g), (201, 2048 + g), (7, 4096 + g)):
+        for n, k in ((1, g), (3, 3 * g), (201, 2048 + g), (7, 4096 + g), (5, 8192 + 3 * g)):
             r = qweight(O, n, k, nbits, g, zero_bits, 31 * n + k + nbits)
             x16 = synth.half_bits(synth.student_t_weights(m, k, 7 + m + k)).reshape(-1)
             for shift in (0, 4, 1):
