@@ -1,6 +1,7 @@
 // hqq_aux.hip -- zero-point requantization, dequantization, pack and unpack for gfx950.
 //
-// Packed layout (the pages name only the containers): a flat code stream in memory order,
+// Packed layout (the pages list the bit widths 8/4/3/2/1 and give no layout; the containers
+// are this library's choice): a flat code stream in memory order,
 // code k of a container in bits [nbits*k, nbits*k + nbits); uint8 containers for 8/4/2/1
 // bits, little-endian uint32 containers of ten 3-bit codes with bits 30-31 zero.
 #include <hip/hip_runtime.h>

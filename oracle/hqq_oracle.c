@@ -26,9 +26,9 @@
  * fma / fmaf only where a step says so; every sum is taken sequentially in index order.
  * Inputs must be finite (asserted).
  *
- * Parity pins for every function here live in the test suite; the one regime with no
- * closed form (active shrink with p < 1) is "parity unpinned" beyond the invariants the
- * tests check (shrink formula, monotone accepted error).
+ * Parity pins for every function here live in the test suite. The regime with no closed
+ * form (a live shrink, W_e != 0) is pinned trace for trace against an independent exact
+ * re-statement of the iteration (exact rationals, |r|^(p-1) in 60-digit decimal arithmetic).
  */
 #include <assert.h>
 #include <math.h>
@@ -349,11 +349,11 @@ void hqo_zero_to_half(const float *z, int64_t n, uint16_t *zh)
 }
 
 /* ------------------------------------------------------------------------------------ */
-/* Packed code layout. Reading (the pages name the containers, not the bit order): a flat   */
-/* stream of codes in row-major order; code k of a container occupies bits                 */
-/* [nbits*k, nbits*k + nbits). 8/4/2/1-bit codes fill uint8 containers (1/2/4/8 per byte);  */
-/* 3-bit codes fill little-endian uint32 containers, 10 per word, bits 30-31 zero. Unused   */
-/* trailing bits are zero.                                                                  */
+/* Packed code layout. Reading: the pages list the bit widths 8/4/3/2/1 and give no layout, */
+/* so the containers are this build's choice. A flat stream of codes in row-major order;   */
+/* code k of a container occupies bits [nbits*k, nbits*k + nbits). 8/4/2/1-bit codes fill  */
+/* uint8 containers (1/2/4/8 per byte); 3-bit codes fill little-endian uint32 containers,  */
+/* 10 per word, bits 30-31 zero. Unused trailing bits are zero.                            */
 /* ------------------------------------------------------------------------------------ */
 
 size_t hqo_packed_bytes(int64_t n, int nbits)

@@ -1,15 +1,29 @@
-"""Exact rational re-statement of the HQQ iteration, for pinning the oracle.
+"""Exact re-statement of the HQQ iteration, for pinning the oracle.
 
 Written independently of the oracle's C code: Python Fractions, no floating point except
-the binary32 rounding of the solver state, which is done here by exact nearest-even
-selection. It covers the regime where the shrink output W_e is zero everywhere (the
-auxiliary variable then drops out of the zero update).
+the binary32 rounding of the solver state (scale, zero, beta), which is done here by exact
+nearest-even selection. Two regimes:
+
+* the reduced iteration, where the shrink output W_e is zero everywhere and the auxiliary
+  variable drops out of the zero update (``shrink=False``);
+* the full iteration with a live shrink (``shrink=True``): sub-problem 1 of techreport.ngo
+  "Half-Quadratic Quantization of Large Machine Learning Models", section "Outlier-aware
+  optimization without gradients" -- the generalized soft-threshold
+  W_e = sign(r) * max(|r| - |r|^(p-1)/beta, 0) of the residual r = W - W_r of the accepted
+  iterate -- then sub-problem 2, z = mean(q - (W - W_e) * s), then beta <- beta * kappa (the
+  parameters of its section "Benchmark results / Llama-2"). Every quantity is an exact
+  rational except |r|^(p-1) for p != 1, which is evaluated in 60-digit decimal arithmetic
+  (correctly rounded at that precision), about 40 digits beyond anything binary32 or binary64
+  can resolve.
 """
 from __future__ import annotations
 
+import decimal
 from fractions import Fraction as F
 
 import numpy as np
+
+_DEC = decimal.Context(prec=60, rounding=decimal.ROUND_HALF_EVEN)
 
 
 def f32_round(v: F) -> F:
@@ -34,11 +48,41 @@ def round_half_even(v: F) -> int:
     return round(v)  # Fraction.__round__ rounds half to even
 
 
-def exact_solve(x16: np.ndarray, nbits: int, iters: int = 20, early_stop: bool = True):
-    """Reduced HQQ iteration (W_e = 0) in exact arithmetic with binary32 s and z.
+def _dec(v: F) -> decimal.Decimal:
+    return _DEC.divide(decimal.Decimal(v.numerator), decimal.Decimal(v.denominator))
+
+
+def power(a: F, e: F) -> F:
+    """a**e for a > 0: exact when e == 0, else 60-digit decimal arithmetic."""
+    if e == 0:
+        return F(1)
+    return F(_DEC.power(_dec(a), _dec(e)))
+
+
+def soft_threshold(r: F, p: F, beta: F) -> F:
+    """Generalized soft-threshold sign(r) * max(|r| - |r|^(p-1)/beta, 0); 0 at r = 0 (the
+    operator's limit for p < 1)."""
+    if r == 0:
+        return F(0)
+    a = abs(r)
+    m = a - power(a, p - 1) / beta
+    if m <= 0:
+        return F(0)
+    return m if r > 0 else -m
+
+
+def exact_solve(x16: np.ndarray, nbits: int, iters: int = 20, early_stop: bool = True,
+                shrink: bool = False, p: float = 0.7, beta0: float = 1.0,
+                kappa: float = 1.01):
+    """The HQQ iteration for one group in exact arithmetic with binary32 s, z and beta.
+
+    shrink=False: the reduced iteration (W_e = 0). shrink=True: the full iteration with the
+    generalized soft-threshold of the accepted iterate's residual, beta_t = beta0 * kappa^(t-1)
+    as a sequence of binary32 products, multiplied after the zero update.
 
     Returns codes, s, z, passes (evaluation count incl. the initial one, running on through
-    exact fixed points as the literal loop does), and the list of (S, accepted)."""
+    exact fixed points as the literal loop does), trace (list of (S, accepted)), the zeros
+    visited, and `active` (number of iterations whose W_e had a non-zero entry)."""
     qmax = (1 << nbits) - 1
     xs = [F(float(v)) for v in np.asarray(x16, np.float16)]
     g = len(xs)
@@ -49,33 +93,42 @@ def exact_solve(x16: np.ndarray, nbits: int, iters: int = 20, early_stop: bool =
     s = f32_round(F(qmax) / rng) if rng > 0 else F(1)
     z = f32_round(-(mn32 * s))
     sum_x = sum(xs)
+    p32 = F(float(np.float32(p)))
+    kappa32 = F(float(np.float32(kappa)))
+    beta = F(float(np.float32(beta0)))
 
     def evaluate(z):
-        q = []
-        S = F(0)
+        q, e = [], []
         for x in xs:
             u = x * s + z
             c = min(max(round_half_even(u), 0), qmax)
             q.append(c)
-            S += abs(u - c)
-        return q, S
+            e.append(u - c)
+        return q, e, sum(abs(v) for v in e)
 
-    q, S_best = evaluate(z)
+    q, e, S_best = evaluate(z)
     trace = [(S_best, True)]
     visited = [z]
-    passes = 1
+    passes, active = 1, 0
     for _ in range(iters):
-        z_new = f32_round((F(sum(q)) - s * sum_x) / g)
-        q_new, S_new = evaluate(z_new)
+        if shrink:
+            # residual of the accepted iterate: r = x - (q - z)/s = (x*s + z - q)/s
+            we = [soft_threshold(ej / s, p32, beta) for ej in e]
+            active += any(w != 0 for w in we)
+            z_new = f32_round(sum(qj - (xj - wj) * s for qj, xj, wj in zip(q, xs, we)) / g)
+            beta = f32_round(beta * kappa32)
+        else:
+            z_new = f32_round((F(sum(q)) - s * sum_x) / g)
+        q_new, e_new, S_new = evaluate(z_new)
         visited.append(z_new)
         passes += 1
         if early_stop and S_new > S_best:
             trace.append((S_new, False))
             break
         trace.append((S_new, True))
-        z, q, S_best = z_new, q_new, S_new
+        z, q, e, S_best = z_new, q_new, e_new, S_new
     return dict(codes=np.array(q, np.uint8), s=float(s), z=float(z), passes=passes,
-                trace=trace, visited=[float(v) for v in visited])
+                trace=trace, visited=[float(v) for v in visited], active=active)
 
 
 def shrink_surely_zero(x16: np.ndarray, nbits: int, s: float, zs, p: float, beta_max: float):
