@@ -73,6 +73,8 @@ hqq_status check_job(const hqq_job &j, int idx)
         return fail(HQQ_ERR_ARG, who + "early_stop must be 0 or 1");
     if (j.zero_bits != 8 && j.zero_bits != 16)
         return fail(HQQ_ERR_ARG, who + "zero_bits must be 8 or 16");
+    if (j.rows * j.cols / j.group_size >= (int64_t(1) << 32))
+        return fail(HQQ_ERR_ARG, who + "at most 2^32 - 1 groups per tensor");
     if (j.rows * j.cols == 0) return HQQ_OK;
     if (!j.W || !j.packed || !j.scale || !j.zero)
         return fail(HQQ_ERR_ARG, who + "W, packed, scale and zero must be non-null");
@@ -172,8 +174,8 @@ void make_plan(const hqq_job *jobs, int n_jobs, char *ws, Plan &P)
     off += round_up(sizeof(uint32_t) * 2 * (size_t)(n > 0 ? n : 1));
     P.off_table = off;
     off += round_up(sizeof(hqq::DevJob) * (size_t)(n > 0 ? n : 1));
-    P.off_counters = off;
-    off += round_up(sizeof(uint32_t) * (P.first.size() > 0 ? P.first.size() : 1));
+    P.off_counters = off;                // one tile counter per class, then the status word
+    off += round_up(sizeof(uint32_t) * (P.first.size() + 1));
     P.bytes = n > 0 ? off : 0;
     P.first.push_back(n);
     int64_t item = 0;
@@ -291,7 +293,7 @@ hqq_status run_batch(const hqq_job *jobs, int n_jobs, void *workspace, size_t wo
             f.n = n - o < hqq::kFillJobs ? n - o : hqq::kFillJobs;
             f.offset = o;
             f.counters = counters;
-            f.n_counters = n_classes;
+            f.n_counters = n_classes + 1;
             for (int i = 0; i < f.n; ++i) f.jobs[i] = P.table[o + i];
             hipError_t e = hqq::launch_fill(f, table, s);
             if (e != hipSuccess) return device_fail(e, "job table launch");
@@ -308,6 +310,7 @@ hqq_status run_batch(const hqq_job *jobs, int n_jobs, void *workspace, size_t wo
             a.iters = j.iters;
             a.early_stop = j.early_stop;
             a.counter = counters + c;
+            a.status = counters + n_classes;
             hipError_t e = hqq::launch_stream(a, j.nbits, j.group_size, s);
             if (e != hipSuccess) return device_fail(e, "solver launch");
         }
@@ -420,6 +423,38 @@ hqq_status hqq_requant_batch(const hqq_job *jobs, int n_jobs, void *workspace,
     return run_batch(jobs, n_jobs, workspace, workspace_bytes, stream, kRequant);
 }
 
+hqq_status hqq_batch_check(const hqq_job *jobs, int n_jobs, const void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    hqq_status st = check_batch(jobs, n_jobs, const_cast<void *>(workspace), workspace_bytes);
+    if (st != HQQ_OK) return st;
+    Plan P;
+    make_plan(jobs, n_jobs, nullptr, P);
+    if (P.table.empty()) {
+        g_last_error.clear();
+        return HQQ_OK;
+    }
+    const int n_classes = (int)P.first.size() - 1;
+    const uint32_t *status =
+        reinterpret_cast<const uint32_t *>(static_cast<const char *>(workspace) + P.off_counters) +
+        n_classes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t flag = 0;
+    hipError_t e = hipMemcpyAsync(&flag, status, sizeof(flag), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return device_fail(e, "batch check");
+    if (flag & 1u)
+        return fail(HQQ_ERR_DEVICE, "the solver ran out of its step budget: some groups of this "
+                                    "batch were not written");
+    g_last_error.clear();
+    return HQQ_OK;
+}
+
+void hqq_debug_solver(int64_t step_budget, int pass_layout)
+{
+    hqq::set_solver_debug(step_budget, pass_layout);
+}
+
 size_t hqq_streamed_workspace_bytes(const hqq_job *jobs, int n_jobs, size_t staging_bytes)
 {
     if (n_jobs < 0 || (n_jobs > 0 && !jobs) || n_jobs > 65535) return SIZE_MAX;
@@ -459,18 +494,22 @@ hqq_status hqq_quantize_streamed(const hqq_job *jobs, int n_jobs, void *staging,
         return fail(HQQ_ERR_ARG, "workspace must be 256-byte aligned");
 
     hipStream_t s = static_cast<hipStream_t>(stream), cs = static_cast<hipStream_t>(copy_stream);
-    // copied[h]: half h holds its chunk; consumed[h]: the solve of half h's chunk is done
-    hipEvent_t copied[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr};
-    hipError_t e = hipSuccess;
+    // copied[h]: half h holds its chunk; consumed[h]: the solve of half h's chunk is done;
+    // entry: all work enqueued on `stream` before this call (a previous call's solves may
+    // still read either half)
+    hipEvent_t copied[2] = {nullptr, nullptr}, consumed[2] = {nullptr, nullptr}, entry = nullptr;
+    hipError_t e = hipEventCreateWithFlags(&entry, hipEventDisableTiming);
     for (int h = 0; h < 2 && e == hipSuccess; ++h) {
         e = hipEventCreateWithFlags(&copied[h], hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&consumed[h], hipEventDisableTiming);
     }
+    if (e == hipSuccess) e = hipEventRecord(entry, s);
     auto release = [&]() {                       // safe while recorded work is pending
         for (int h = 0; h < 2; ++h) {
             if (copied[h]) (void)hipEventDestroy(copied[h]);
             if (consumed[h]) (void)hipEventDestroy(consumed[h]);
         }
+        if (entry) (void)hipEventDestroy(entry);
     };
     if (e != hipSuccess) {
         release();
@@ -483,6 +522,7 @@ hqq_status hqq_quantize_streamed(const hqq_job *jobs, int n_jobs, void *staging,
         const int h = (int)(k % 2);
         char *dst = static_cast<char *>(staging) + h * half;
         if (k >= 2) e = hipStreamWaitEvent(cs, consumed[h], 0);   // chunk k-2 left this half
+        else e = hipStreamWaitEvent(cs, entry, 0);                  // earlier work left it
         local.assign(jobs + c.first, jobs + c.first + c.count);
         size_t off = 0;
         for (int i = 0; i < c.count && e == hipSuccess; ++i) {

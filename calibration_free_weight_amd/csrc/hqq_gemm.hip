@@ -1033,7 +1033,7 @@ void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t 
                hipStream_t stream)
 {
     const dim3 block(256);
-    if (M > kWsM && Wr) {
+    if (M > kWsM && Wr && recon_fits(w.packed, NB, w.K, 1, Wr)) {   // packed aligned for its loads
         launch_recon_nb<NB>(w, w.N * w.K, w.K, 1, false, Wr, stream);   // N*K: a multiple of 16
         launch_f16(X, M, Wr, w.N, w.K, Y, stream);
     } else if (M > kSkinnyLo && 64 * w.K * 2 < 0x7FFFFFF0 &&

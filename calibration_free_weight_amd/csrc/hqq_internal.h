@@ -35,7 +35,17 @@ struct StreamArgs {
     int iters, early_stop;
     uint32_t *counter;          // tile claim counter, zero before the launch
     uint32_t chunk;             // tiles per claim
+    uint32_t *status;           // bit 0 set by a wave that ran out of its step budget
+    int64_t budget0;            // a wave's loop-step budget at start
+    int64_t budget_tile;        // and what each tile it takes in adds
 };
+
+// Diagnostic settings of the solver launches. Step budget of the waves: 0 selects the
+// default (a bound the schedule never reaches); a positive value replaces the starting
+// budget and stops its growth per tile. Pass layout: 0 chosen by size, 1 wide, 2 narrow.
+void set_solver_debug(int64_t steps, int layout);
+int64_t step_budget();
+int solver_layout();
 
 constexpr int kFillJobs = 24;   // job descriptors per table-fill launch (kernel arguments)
 struct FillArgs {

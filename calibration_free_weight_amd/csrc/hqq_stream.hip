@@ -46,6 +46,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "hqq_internal.h"
 
 namespace hqq {
@@ -176,12 +178,21 @@ __device__ __forceinline__ uint32_t meta_t(uint32_t m) { return (m >> 8) & 0xffu
 __device__ __forceinline__ uint32_t meta_job(uint32_t m) { return m >> 16; }
 __device__ __forceinline__ uint32_t with_fl(uint32_t m, uint32_t fl) { return (m & ~0xffu) | fl; }
 
-template <int NBITS, int G>
+// Pass layouts. Wide (the default): a lane owns a group (a lane pair when G = 256), which
+// keeps the pass free of cross-lane reductions. Narrow: several lanes share a group (16
+// weights each up to g64, 32 above; 4 lanes at g64 and g128), for tensors too small to give
+// every lane of the machine several groups: a pass then takes a quarter of the time, so the
+// last groups of a launch, which decide its length, finish sooner.
+template <int G> constexpr int wide_ep() { return G <= 128 ? G : 128; }
+template <int G> constexpr int narrow_ep() { return G <= 16 ? G : (G <= 64 ? 16 : 32); }
+
+template <int NBITS, int G, int EP_ = wide_ep<G>()>
 struct Cfg {
-    // Pass layout: a lane owns a group (a lane pair when G = 256), EP weights per lane.
-    static constexpr int EP = G <= 128 ? G : 128;
-    static constexpr int KP = G / EP;               // lanes per group in a pass (1 or 2)
+    // Pass layout: KP lanes per group, EP weights per lane.
+    static constexpr int EP = EP_;
+    static constexpr int KP = G / EP;               // lanes per group in a pass
     static constexpr int WP = EP / 2;               // binary16 pairs per lane
+    static constexpr bool NARROW = EP < wide_ep<G>();
     // Batch layout (INIT, EXACT, EPILOGUE): KB lanes per group, EB weights per lane.
     static constexpr int EB = G >= 32 ? 32 : 16;
     static constexpr int KB = G / EB;
@@ -194,7 +205,11 @@ struct Cfg {
     // weights and 48 bytes of state, the rings and the 3-bit code stage; at most three
     // batches of slots.
     // (3-bit g32 stays at three: its code stage leaves fewer slots than four waves need.)
-    static constexpr int WAVES = (G <= 16 || (G == 32 && NBITS != 3)) ? 4 : (G <= 128 ? 3 : 2);
+    // The narrow layout holds 8 or 16 weight registers per lane and runs four waves (three
+    // for 3-bit g32 and g256, whose slot pools would not fit four).
+    static constexpr int WAVES =
+        NARROW ? (NBITS == 3 && (G == 32 || G >= 256) ? 3 : 4)
+               : ((G <= 16 || (G == 32 && NBITS != 3)) ? 4 : (G <= 128 ? 3 : 2));
     static constexpr int RC = GB >= 32 ? 128 : 64;  // ring capacity
     static constexpr int LDS_WAVE = 163840 / (4 * WAVES) / 1280 * 1280;
     static constexpr int LDS_FREE = LDS_WAVE - 4 * RC - (NBITS == 3 ? 64 * EB : 0) - 128;
@@ -202,7 +217,7 @@ struct Cfg {
     // exchanges (half the swaps, measured 10-13 % faster at g16-g64); larger groups move with
     // 16-byte stores and loads through free slots and a spare slot (the exchanges of 256-byte
     // groups measured 1.5-3 % slower at g128).
-    static constexpr bool XCHG = G <= 64;
+    static constexpr bool XCHG = G <= 64 && KP == 1;
     static_assert(!XCHG || KP == 1, "in-place swaps move one lane per group");
     // one more column of weights (for an odd stride) comes out of the budget first, and with
     // the spare slot two whole slots
@@ -271,10 +286,9 @@ struct Exact {
 
 // Exact (binary64) evaluation of one batch lane's EB weights (chunks c0.. of slot j) at zero
 // z. Rare: a rolled loop, so it adds few registers to the binary32 path.
-template <int NBITS, int G>
+template <class C>
 __device__ __forceinline__ Exact eval_exact(const uint16_t *xs, int j, int c0, float s, float z)
 {
-    using C = Cfg<NBITS, G>;
     const double sd = s, zd = z, qm = C::QMAX;
     double s_ = 0.0, q_ = 0.0, d_ = 0.0;
 #pragma unroll 1
@@ -296,12 +310,12 @@ struct Advance {
     uint8_t out;
     float zn;
 };
-template <int NBITS, int G>
+template <class C>
 __device__ __forceinline__ Advance advance_core(int t, int iters, float s, float zb, float Qb,
                                                 float Db, bool sbx, double X, float beta,
                                                 float tau_min, double tau_exp)
 {
-    using C = Cfg<NBITS, G>;
+    constexpr int G = C::KB * C::EB;
     if (t > iters) return Advance{kDone, zb};
     // Dead zone of the shrink: max|r| = max|u - q|/s <= beta^(-1/(2-p)), tested with a
     // relative margin of 4e-6 that covers the binary32 rounding of the products. The
@@ -319,11 +333,11 @@ __device__ __forceinline__ Advance advance_core(int t, int iters, float s, float
     return Advance{kNext, zn};
 }
 
-template <int NBITS, int G>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Cfg<NBITS, G>::WAVES)))
+template <int NBITS, int G, int EPL>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Cfg<NBITS, G, EPL>::WAVES)))
 stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 {
-    using C = Cfg<NBITS, G>;
+    using C = Cfg<NBITS, G, EPL>;
     constexpr int KP = C::KP, WP = C::WP, EB = C::EB, KB = C::KB, GB = C::GB, WB = C::WB;
     constexpr int NS = C::NS, RM = C::RC - 1;
     static_assert(NS <= 255, "slot indices are bytes");
@@ -447,7 +461,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     auto advance_slot = [&](uint8_t j, float s, float zb, float Qb, float Db, bool sbx) -> uint8_t {
         const uint32_t m = st_b[j].meta;
         const int t = (int)meta_t(m);
-        const Advance ad = advance_core<NBITS, G>(t, a.iters, s, zb, Qb, Db, sbx, st_c[j].X,
+        const Advance ad = advance_core<C>(t, a.iters, s, zb, Qb, Db, sbx, st_c[j].X,
                                                   st_b[j].beta, tau_min, tau_exp);
         if (bleader) {
             if (ad.out == kDone) st_a[j].zb = ad.zn;
@@ -670,8 +684,10 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     };
 
     // A bound on loop steps that the schedule never reaches (every step moves at least one
-    // group forward): a defect would end the launch instead of hanging it.
-    int64_t budget = 1024;
+    // group forward): a defect ends the launch instead of hanging it, and the wave that runs
+    // out sets the launch's status flag so that the host can report incomplete outputs.
+    int64_t budget = a.budget0;
+    bool ran_out = false;
 
     prefetch();
 
@@ -686,6 +702,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             // SIMD's other waves fill the gaps. Measured 1-5 % faster than one level.
             __builtin_amdgcn_s_setprio(1);
             if (--budget <= 0) {
+                ran_out = true;
                 done = true;
                 break;
             }
@@ -873,13 +890,13 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                     const int c0 = sub * (EB / 8);
                     if (((fl >> 1) & 3) == kDecide) {
                         const float z = sa.z;
-                        const Exact xn = eval_exact<NBITS, G>(xs, j, c0, s, z);
+                        const Exact xn = eval_exact<C>(xs, j, c0, s, z);
                         const double S = addd_k<KB>(xn.S);
                         const float Q = (float)addd_k<KB>(xn.Q);
                         const float D = maxf_k<KB>((float)xn.D);
                         double Sb = st_c[j].Sb;
                         if (!(fl & kFirst) && !(fl & kSbExact))
-                            Sb = addd_k<KB>(eval_exact<NBITS, G>(xs, j, c0, s, sa.zb).S);
+                            Sb = addd_k<KB>(eval_exact<C>(xs, j, c0, s, sa.zb).S);
                         if ((fl & kFirst) || !a.early_stop || S <= Sb) {
                             if (bleader) {
                                 st_a[j].zb = z;
@@ -939,10 +956,10 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 if (status == kActive) {
                     float S, T, D;
                     eval_fast<NBITS, WP>(xr, g_s, g_z, S, T, D);
-                    if (KP == 2) {
-                        S = addf_k<2>(S);
-                        T = addf_k<2>(T);
-                        D = maxf_k<2>(D);
+                    if (KP > 1) {              // butterflies: every lane of the group gets
+                        S = addf_k<KP>(S);     // the same sums, so all take the same decision
+                        T = addf_k<KP>(T);
+                        D = maxf_k<KP>(D);
                     }
                     const float Q = (float)rint(fma((double)G, (double)g_z, g_X) - (double)T);
                     const uint32_t fl = meta_fl(g_meta);
@@ -974,7 +991,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                         g_Sb = S;
                         g_Db = D;
                         g_meta = with_fl(g_meta, 0);
-                        const Advance ad = advance_core<NBITS, G>((int)meta_t(g_meta), a.iters, g_s, g_z, Q, D,
+                        const Advance ad = advance_core<C>((int)meta_t(g_meta), a.iters, g_s, g_z, Q, D,
                                                                   false, g_X, g_beta, tau_min,
                                                                   tau_exp);
                         if (ad.out == kDone) {
@@ -1010,7 +1027,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
         }
         // ================= INIT: a prefetched tile becomes ready groups ===============
         __builtin_amdgcn_s_setprio(0);
-        budget += 8 * (int64_t)(a.iters + 4) * GB;
+        budget += a.budget_tile;
         const int nv = pf_nv;
         const bool valid = k < nv;
         uint8_t j = 0;
@@ -1062,23 +1079,21 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
         prefetch();
     }
     flush_minmax();
+    if (ran_out && lane == 0)   // set after the loop: inside it the atomic costs registers
+        __hip_atomic_fetch_or(gbl(a.status), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NBITS, int G>
-hipError_t launch_one(const StreamArgs &args, hipStream_t stream)
+template <int NBITS, int G, int EPL>
+hipError_t launch_layout(StreamArgs a, int cus, hipStream_t stream)
 {
-    if (args.n_tiles == 0) return hipSuccess;
-    StreamArgs a = args;
+    using C = Cfg<NBITS, G, EPL>;
+    const int64_t fixed = step_budget();
+    a.budget0 = fixed > 0 ? fixed : 1024;
+    a.budget_tile = fixed > 0 ? 0 : 8 * (int64_t)(a.iters + 4) * C::GB;
     // Persistent grid: as many single-wave workgroups as the LDS pool lets the CUs hold; tiles
     // are claimed in chunks small enough to balance the waves (about 16 claims per wave).
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-    }
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel<NBITS, G>, 64, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel<NBITS, G, EPL>, 64, 0) !=
             hipSuccess || per_cu <= 0)
         per_cu = 4;
     const int64_t waves = (int64_t)cus * per_cu;
@@ -1087,9 +1102,32 @@ hipError_t launch_one(const StreamArgs &args, hipStream_t stream)
     a.chunk = (uint32_t)chunk;
     const int64_t claims = (a.n_tiles + chunk - 1) / chunk;
     const int64_t grid = waves < claims ? waves : claims;
-    hipLaunchKernelGGL((stream_kernel<NBITS, G>), dim3((unsigned)grid), dim3(64), 0, stream, a,
-                       a.jobs);
+    hipLaunchKernelGGL((stream_kernel<NBITS, G, EPL>), dim3((unsigned)grid), dim3(64), 0, stream,
+                       a, a.jobs);
     return hipGetLastError();
+}
+
+template <int NBITS, int G>
+hipError_t launch_one(const StreamArgs &a, hipStream_t stream)
+{
+    if (a.n_tiles == 0) return hipSuccess;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+    }
+    if constexpr (narrow_ep<G>() == wide_ep<G>()) {
+        return launch_layout<NBITS, G, wide_ep<G>()>(a, cus, stream);
+    } else {
+        // Narrow when the class's groups would give each lane of the machine fewer than
+        // about four (the wide layout holds up to 12 waves of 64 groups per compute unit).
+        const int64_t groups = a.n_tiles * Cfg<NBITS, G>::GB;
+        const int mode = solver_layout();
+        const bool narrow = mode == 2 || (mode == 0 && groups < 4 * (int64_t)cus * 12 * 64);
+        if (narrow) return launch_layout<NBITS, G, narrow_ep<G>()>(a, cus, stream);
+        return launch_layout<NBITS, G, wide_ep<G>()>(a, cus, stream);
+    }
 }
 
 template <int NBITS>
@@ -1120,7 +1158,18 @@ __global__ void fill_kernel(FillArgs f, DevJob *table)
         for (int c = i; c < f.n_counters; c += blockDim.x) f.counters[c] = 0u;
 }
 
+std::atomic<int64_t> g_step_budget{0};
+std::atomic<int> g_layout{0};
+
 }  // namespace
+
+void set_solver_debug(int64_t steps, int layout)
+{
+    g_step_budget.store(steps > 0 ? steps : 0);
+    g_layout.store(layout == 1 || layout == 2 ? layout : 0);
+}
+int64_t step_budget() { return g_step_budget.load(); }
+int solver_layout() { return g_layout.load(); }
 
 int64_t tiles_for(int64_t n_groups, int g)
 {

@@ -21,7 +21,7 @@ EXPORTS = ("hqq_packed_bytes", "hqq_workspace_bytes", "hqq_quantize", "hqq_quant
            "hqq_streamed_workspace_bytes", "hqq_dequantize", "hqq_gemm",
            "hqq_gemm_workspace_bytes", "hqq_gemm_f16", "hqq_requant_scales",
            "hqq_dequantize_scales", "hqq_pack", "hqq_unpack", "hqq_status_string",
-           "hqq_last_error")
+           "hqq_last_error", "hqq_batch_check", "hqq_debug_solver")
 
 
 class HQQError(RuntimeError):
@@ -60,6 +60,10 @@ def lib():
         for name in ("hqq_quantize_batch", "hqq_solve_batch", "hqq_requant_batch"):
             getattr(L, name).restype = i32
             getattr(L, name).argtypes = [C.POINTER(hqq_job), i32, vp, C.c_size_t, vp]
+        L.hqq_batch_check.restype = i32
+        L.hqq_batch_check.argtypes = [C.POINTER(hqq_job), i32, vp, C.c_size_t, vp]
+        L.hqq_debug_solver.restype = None
+        L.hqq_debug_solver.argtypes = [i64, i32]
         L.hqq_quantize_streamed.restype = i32
         L.hqq_quantize_streamed.argtypes = [C.POINTER(hqq_job), i32, vp, C.c_size_t, vp,
                                             C.c_size_t, vp, vp]
@@ -162,6 +166,18 @@ def hqq_solve_batch(jobs, workspace, stream=None) -> None:
 
 def hqq_requant_batch(jobs, workspace, stream=None) -> None:
     _batch(lib().hqq_requant_batch, jobs, workspace, stream)
+
+
+def hqq_batch_check(jobs, workspace, stream=None) -> None:
+    """Waits for `stream`; raises HQQError (HQQ_ERR_DEVICE) if the last solve on this
+    workspace left groups unwritten."""
+    _batch(lib().hqq_batch_check, jobs, workspace, stream)
+
+
+def hqq_debug_solver(step_budget: int = 0, pass_layout: int = 0) -> None:
+    """Test hook: a fixed solver step budget (0 = default) and the pass layout (0 = by
+    size, 1 = one lane per group, 2 = several lanes per group)."""
+    lib().hqq_debug_solver(int(step_budget), int(pass_layout))
 
 
 def hqq_streamed_workspace_bytes(jobs, staging_bytes) -> int:
@@ -275,4 +291,5 @@ def quantize(W, nbits, group_size, axis=1, p=0.7, beta=1.0, kappa=1.01, iters=20
                  out["packed"], out["scale"], out["zero"], out["zero_meta"], out["passes"],
                  ws, stream)
     out["workspace"] = ws
+    out["job"] = job
     return out

@@ -19,7 +19,8 @@
  *  - Tensor pointers are DEVICE pointers owned by the caller. The library allocates no
  *    memory and keeps no state between calls; scratch space is the caller's `workspace`.
  *  - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue work on it and
- *    never synchronise; a device fault surfaces at the caller's next synchronisation.
+ *    never synchronise (the one exception, hqq_batch_check, says so); a device fault
+ *    surfaces at the caller's next synchronisation.
  *  - Arguments are validated on the host before any HIP call. A rejected call returns a
  *    non-zero hqq_status, enqueues nothing and leaves a message in hqq_last_error().
  *  - Inputs must be finite; results for NaN/Inf weights are unspecified.
@@ -31,7 +32,9 @@
  *    W[b*g .. b*g+g-1][j], and per-group outputs (scale, zero, passes) form a row-major
  *    [rows/g, cols] array (group (b, j) at b*cols + j). Either way the codes keep W's
  *    row-major order.
- *  - Packed codes: one flat stream in memory order; code k of a container occupies bits
+ *  - Packed codes. The pages list the bit widths 8/4/3/2/1 [SK "HQQ - Half-Quadratic
+ *    Quantization", introduction] and give no storage layout; this one is the library's
+ *    choice. One flat stream in memory order; code k of a container occupies bits
  *    [nbits*k, nbits*k + nbits). 8/4/2/1-bit codes fill uint8 containers (1/2/4/8 per byte);
  *    3-bit codes fill little-endian uint32 containers, 10 per word, bits 30-31 zero.
  *    Unused trailing bits are zero. Size: hqq_packed_bytes(rows*cols, nbits).
@@ -76,8 +79,10 @@ typedef struct hqq_job {
     uint8_t *passes;         /* out, nullable: evaluations run per group (instrumentation)  */
 } hqq_job;
 
-/* Bytes of the packed code stream for n_codes codes of nbits bits (0 for invalid nbits):
- * ceil(n*nbits/8) for 8/4/2/1 bits, 4*ceil(n/10) for 3 bits. */
+/* Bytes of the packed code stream (the layout under "Packed codes" above, for the pages'
+ * bit widths 8/4/3/2/1 [SK introduction]) for n_codes codes of nbits bits, 0 for any other
+ * nbits or n_codes < 0: ceil(n*nbits/8) for 8/4/2/1 bits, 4*ceil(n/10) for 3 bits. Host
+ * only; never fails otherwise. */
 size_t hqq_packed_bytes(int64_t n_codes, int nbits);
 
 /* Workspace bytes hqq_quantize_batch needs for these jobs (host array): the device copy of
@@ -123,6 +128,26 @@ hqq_status hqq_solve_batch(const hqq_job *jobs, int n_jobs, void *workspace,
 hqq_status hqq_requant_batch(const hqq_job *jobs, int n_jobs, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* Completion check of the last solve on a workspace. Every solver wave bounds its loop
+ * steps by a budget the schedule never reaches, so that a defect ends the launch instead of
+ * hanging it; a wave that runs out sets a status word in the workspace (cleared by the next
+ * solve on that workspace) and leaves some groups of the batch unwritten. This call takes
+ * the same jobs and workspace as the solve, waits for `stream` to complete (it is the one
+ * synchronising call of this library), and returns HQQ_ERR_DEVICE with a message when the
+ * flag is set or the stream reports an error, HQQ_OK otherwise. Argument errors as for
+ * hqq_quantize_batch. */
+hqq_status hqq_batch_check(const hqq_job *jobs, int n_jobs, const void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Diagnostic hook for tests; the settings apply to every solver launch made afterwards, by
+ * any thread. step_budget > 0 gives each solver wave a fixed budget of that many loop steps
+ * (0 restores the default): with a small budget the solver ends early, every wave still
+ * exits normally, and hqq_batch_check reports the incomplete batch. pass_layout selects how
+ * lanes share a group during the solver's passes: 0 by the size of the batch (the default),
+ * 1 one lane per group (wide), 2 several lanes per group (narrow, the layout for small
+ * tensors); results are identical, only the speed differs. */
+void hqq_debug_solver(int64_t step_budget, int pass_layout);
+
 /* Quantize a batch whose weights live in HOST memory, for stacks larger than the device
  * memory [SK "Common issues": when quantization runs out of memory, load the layers one after
  * another; TR "Speed: from hours to minutes": each weight crosses to the GPU once]. jobs[i].W is a host pointer (allocate it pinned, e.g. with
@@ -132,10 +157,11 @@ hqq_status hqq_requant_batch(const hqq_job *jobs, int n_jobs, void *workspace,
  * 256-byte aligned; each tensor takes 2*rows*cols bytes rounded up to 256): chunk k is
  * copied into half k % 2 on `copy_stream` while chunk k-1 is solved on `stream`.
  * `workspace` must hold hqq_streamed_workspace_bytes(jobs, n_jobs, staging_bytes). The
- * call enqueues only (it creates four HIP events and releases them before returning); the
+ * call enqueues only (it creates five HIP events and releases them before returning); the
  * host weights must stay valid and unchanged until `stream` has completed the work. A
  * tensor larger than half the staging buffer -> HQQ_ERR_WORKSPACE. copy_stream may equal
- * stream (no overlap). */
+ * stream (no overlap). The first copy into each half waits for all work enqueued on
+ * `stream` before the call, so consecutive calls may share one staging buffer. */
 hqq_status hqq_quantize_streamed(const hqq_job *jobs, int n_jobs, void *staging,
                                  size_t staging_bytes, void *workspace, size_t workspace_bytes,
                                  void *stream, void *copy_stream);
@@ -185,7 +211,7 @@ hqq_status hqq_dequantize_scales(const uint8_t *scale_q, const void *scale_meta,
  * binary16 matrix-core GEMM reads it (the faster choice for large M); NULL keeps the
  * streaming kernels. A non-NULL workspace that is too small is HQQ_ERR_WORKSPACE. Its
  * contents are scratch; calls that share one race. Packed buffers that are not 4-byte
- * aligned (8 bytes at 8 bits) take slower fallback kernels. */
+ * aligned (8 bytes at 8 bits) take slower fallback kernels, with or without a workspace. */
 hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *scale,
                     const void *zero, const void *zero_meta, int64_t N, int64_t K, int nbits,
                     int group_size, int zero_bits, void *Y, void *workspace,
@@ -206,13 +232,20 @@ size_t hqq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hqq_status hqq_gemm_f16(const void *X, int64_t M, const void *Wr, int64_t N, int64_t K, void *Y,
                         void *stream);
 
-/* Pack n_codes uint8 codes (each < 2^nbits) into the packed layout above; `packed` must be
- * 16-byte aligned and hold hqq_packed_bytes(n_codes, nbits) bytes. Codes >= 2^nbits are
- * masked to their low nbits bits. */
+/* The bit-packing of the quantized weight W_q [SK "HQQLinear layer": W_q holds the packed
+ * codes; bit widths 8/4/3/2/1 from its introduction], standalone: pack n_codes uint8 codes
+ * (device, each < 2^nbits) into the layout under "Packed codes" above. `packed` (device,
+ * caller-owned) must be 16-byte aligned and hold hqq_packed_bytes(n_codes, nbits) bytes; the
+ * unused bits of the last container are written as zero and nothing past it is touched.
+ * Codes >= 2^nbits are masked to their low nbits bits. nbits outside {1,2,3,4,8},
+ * n_codes < 0, null pointers or a misaligned `packed` -> HQQ_ERR_ARG; n_codes = 0 does
+ * nothing. Enqueues one kernel on `stream`. */
 hqq_status hqq_pack(const uint8_t *codes, int64_t n_codes, int nbits, void *packed,
                     void *stream);
 
-/* Inverse of hqq_pack: n_codes uint8 codes out. */
+/* Inverse of hqq_pack [same passages]: reads hqq_packed_bytes(n_codes, nbits) bytes of
+ * `packed` (device; 4-byte aligned for 3 bits) and writes n_codes uint8 codes (device,
+ * caller-owned) in stream order. Argument errors as for hqq_pack. */
 hqq_status hqq_unpack(const void *packed, int64_t n_codes, int nbits, uint8_t *codes,
                       void *stream);
 

@@ -26,3 +26,16 @@ def has_gpu() -> bool:
         return torch.cuda.is_available()
     except Exception:
         return False
+
+
+@pytest.fixture
+def progress(request):
+    """A function that prints a line at once, past pytest's output capture (long tests show
+    that they are working)."""
+    capman = request.config.pluginmanager.getplugin("capturemanager")
+
+    def emit(msg: str) -> None:
+        with capman.global_and_fixture_disabled():
+            sys.stderr.write(msg + "\n")
+            sys.stderr.flush()
+    return emit

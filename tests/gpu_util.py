@@ -80,3 +80,43 @@ def compare(O, W, out, nbits, g, zero_bits, exact=True, params=None, label=""):
             assert np.array_equal(got[ok], ref["evals_needed"][ok]), \
                 f"{label}: {(got[ok] != ref['evals_needed'][ok]).sum()} pass counts differ"
     return ref
+
+
+def compare_whole(O, pool, W, out, nbits, g, zero_bits, zero32=None, label=""):
+    """Element-by-element comparison of one whole tensor's outputs with the oracle, its
+    groups solved by `pool` (the single-threaded oracle in several processes): packed
+    bytes, scales, zeros (binary16, or uint8 codes and their binary16 step/base), the
+    binary32 zeros when `zero32` is given, and the evaluation counts of groups whose shrink
+    stayed dead. Returns the oracle result."""
+    w16 = u16(W)
+    n = w16.size
+    ng = n // g
+    ref = pool.solve_groups(w16, g, nbits)
+    nb = O.packed_bytes(n, nbits)
+    packed = u8(out["packed"])[:nb]
+    ref_packed = O.pack(ref["codes"], nbits)
+    if not np.array_equal(packed, ref_packed):
+        codes = O.unpack(packed, n, nbits)
+        bad = np.flatnonzero(codes != ref["codes"])
+        raise AssertionError(f"{label}: {bad.size} of {n} codes differ (first at {bad[:5]})")
+    scale = u16(out["scale"])
+    assert np.array_equal(scale, ref["scale"]), \
+        f"{label}: {(scale != ref['scale']).sum()} scales differ"
+    if zero32 is not None:
+        z32 = zero32.detach().cpu().numpy().reshape(-1)[:ng]
+        assert np.array_equal(z32.view(np.uint32), ref["zero_f32"].view(np.uint32)), \
+            f"{label}: {(z32 != ref['zero_f32']).sum()} binary32 zeros differ"
+    if zero_bits == 16:
+        zero = u16(out["zero"])
+        assert np.array_equal(zero, O.zero_to_half(ref["zero_f32"])), f"{label}: zeros differ"
+    else:
+        zq, meta = O.zero_requant(ref["zero_f32"])
+        got = u8(out["zero"])
+        assert np.array_equal(got, zq), f"{label}: {(got != zq).sum()} 8-bit zeros differ"
+        assert np.array_equal(u16(out["zero_meta"]), meta), f"{label}: zero meta differs"
+    if out.get("passes") is not None:
+        ok = ref["shrink_active"] == 0
+        got = u8(out["passes"])
+        assert np.array_equal(got[ok], ref["evals_needed"][ok]), \
+            f"{label}: {(got[ok] != ref['evals_needed'][ok]).sum()} evaluation counts differ"
+    return ref

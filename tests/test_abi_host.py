@@ -56,6 +56,7 @@ BAD = [
     (dict(kappa=-1.0), 1), (dict(iters=-1), 1), (dict(iters=255), 1), (dict(early_stop=2), 1),
     (dict(zero_bits=4), 1), (dict(W=None), 1), (dict(zero_meta=None), 1),
     (dict(W=0x1002), 1), (dict(packed=0x2008), 1), (dict(rows=-1), 1),
+    (dict(rows=1 << 20, cols=1 << 18, group_size=64), 1),    # 2^32 groups
 ]
 
 
@@ -69,6 +70,7 @@ def test_invalid_arguments_rejected(H, kw, status):
     assert H.hqq_status_string(st) != "unknown status"
     arr = (H.hqq_job * 1)(j)
     assert L.hqq_workspace_bytes(arr, 1) == 2 ** 64 - 1
+    assert L.hqq_batch_check(C.byref(j), 1, None, 0, None) == status
 
 
 def test_workspace_sizing_and_check(H):

@@ -98,6 +98,12 @@ def test_axis0_and_axis1_in_one_batch(O, dev):
             ref = O.quantize(u16(W), g, nbits, zero_bits=zb)
             assert np.array_equal(u8(o["packed"])[:ref["packed"].size], ref["packed"]), label
             assert np.array_equal(u16(o["scale"]), ref["scale"]), label
+            zero = u16(o["zero"]) if zb == 16 else u8(o["zero"])
+            assert np.array_equal(zero, ref["zero"]), label
+            if zb == 8:
+                assert np.array_equal(u16(o["zero_meta"]), ref["zero_meta"]), label
+            ok = ref["shrink_active"] == 0
+            assert np.array_equal(u8(o["passes"])[ok], ref["evals_needed"][ok]), label
 
 
 def test_axis0_stack_sampled(O, dev):

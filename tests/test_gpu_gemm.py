@@ -134,18 +134,23 @@ def test_gemm_unaligned_packed_fallback(O, dev, nbits, g, zero_bits):
     # ones (per-row decode for M <= 8, LDS-staged tiles above) take every M
     n, k = 131, 1024 + g
     r = qweight(O, n, k, nbits, g, zero_bits, 41 + nbits)
-    for m in (3, 9, 100):
-        label = f"unaligned m={m} nbits={nbits} g={g} zb={zero_bits}"
+    for m, with_ws in ((3, False), (9, False), (100, False), (100, True)):
+        # with a workspace, M = 100 would reconstruct once; an unaligned packed buffer must
+        # keep it off that path's word loads
+        label = f"unaligned m={m} ws={with_ws} nbits={nbits} g={g} zb={zero_bits}"
         print(label, flush=True)
         x16 = synth.half_bits(synth.student_t_weights(m, k, 9 + m)).reshape(-1)
         X = to_dev(x16, np.int16, dev).view(m, k)
         pk = torch.zeros(r["packed"].size + 16, dtype=torch.uint8, device=dev)
         pk[1:1 + r["packed"].size] = to_dev(r["packed"], np.uint8, dev)
         Y = torch.full((m, n), float("nan"), dtype=torch.float16, device=dev)
+        wb = hqq.hqq_gemm_workspace_bytes(m, n, k)
+        ws = torch.empty(wb, dtype=torch.uint8, device=dev) if with_ws and wb else None
+        assert not with_ws or ws is not None
         hqq.hqq_gemm(X, pk[1:], to_dev(r["scale"], np.int16, dev),
                      to_dev(r["zero"], np.int16 if zero_bits == 16 else np.uint8, dev),
                      None if zero_bits == 16 else to_dev(r["zero_meta"], np.int16, dev),
-                     n, k, nbits, g, zero_bits, Y)
+                     n, k, nbits, g, zero_bits, Y, workspace=ws)
         torch.cuda.synchronize()
         y = u16(Y).view(np.float16).astype(np.float64).reshape(m, n)
         check(O, r, x16, y, m, n, k, g, zero_bits, label)

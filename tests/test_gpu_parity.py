@@ -22,9 +22,11 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run(W, nbits, g, zero_bits=16, passes=True, **params):
+def run(W, nbits, g, zero_bits=16, passes=True, check=True, **params):
     out = hqq.quantize(W, nbits, g, zero_bits=zero_bits, passes=passes, **params)
     torch.cuda.synchronize()
+    if check and out["workspace"] is not None:
+        hqq.hqq_batch_check([out["job"]], out["workspace"])   # no group left unwritten
     return out
 
 
@@ -62,6 +64,27 @@ def test_quantize_matches_oracle(O, dev, nbits, g, zero_bits):
     W = weights(rows, cols, 100 * nbits + g + zero_bits, dev)
     out = run(W, nbits, g, zero_bits)
     compare(O, W, out, nbits, g, zero_bits, label=f"b{nbits} g{g} z{zero_bits}")
+
+
+@pytest.mark.parametrize("layout", [1, 2], ids=["wide", "narrow"])
+@pytest.mark.parametrize("nbits", [1, 2, 3, 4, 8])
+def test_both_pass_layouts(O, dev, nbits, layout):
+    """The solver's two pass layouts (one lane per group; several lanes per group, chosen for
+    small tensors) give identical results: forced here for every bit width and group size,
+    on boundary groups that exercise the exact path and with a live shrink."""
+    try:
+        hqq.hqq_debug_solver(pass_layout=layout)
+        for g in (16, 32, 64, 128, 256):
+            print(f"layout {layout} nbits={nbits} g={g}", flush=True)
+            W = half_grid_groups(40, g * 24, g, nbits, 300 + nbits + g, 0.3).to(dev)
+            for zero_bits in (16, 8):
+                out = run(W, nbits, g, zero_bits)
+                compare(O, W, out, nbits, g, zero_bits, label=f"layout {layout} b{nbits} g{g}")
+            out = run(W, nbits, g, 16, beta=1e4)
+            compare(O, W, out, nbits, g, 16, exact=False, params={"beta": 1e4},
+                    label=f"layout {layout} shrink b{nbits} g{g}")
+    finally:
+        hqq.hqq_debug_solver()
 
 
 @pytest.mark.parametrize("nbits,g", [(4, 64), (2, 16), (3, 64)])
@@ -140,14 +163,39 @@ def test_minimal_staging_pool(O, dev):
     try:
         cases = [(4, 128, 1.0), (4, 128, 0.5), (2, 16, 1.0), (2, 32, 0.5), (3, 32, 1.0),
                  (4, 64, 0.0), (3, 64, 0.3), (8, 256, 0.0)]
-        for nbits, g, frac in cases:
-            print(f"stress pool nbits={nbits} g={g} frac={frac}", flush=True)
-            W = half_grid_groups(48, g * 32, g, nbits, 5 + nbits + g, frac).to(dev)
-            for zero_bits in (16, 8):
-                out = run(W, nbits, g, zero_bits)
-                compare(O, W, out, nbits, g, zero_bits, label=f"stress b{nbits} g{g}")
+        for layout in (1, 2):
+            hqq.hqq_debug_solver(pass_layout=layout)
+            for nbits, g, frac in cases:
+                print(f"stress pool layout={layout} nbits={nbits} g={g} frac={frac}", flush=True)
+                W = half_grid_groups(48, g * 32, g, nbits, 5 + nbits + g, frac).to(dev)
+                for zero_bits in (16, 8):
+                    out = run(W, nbits, g, zero_bits)
+                    compare(O, W, out, nbits, g, zero_bits, label=f"stress b{nbits} g{g}")
     finally:
+        hqq.hqq_debug_solver()
         hqq.LIB_PATH, hqq._L = saved
+
+
+def test_step_budget_exhaustion_is_reported(O, dev):
+    """A solver wave that runs out of its step budget flags the batch: the host sets a tiny
+    budget (every wave still exits normally), and the check reports the incomplete outputs;
+    the next solve on the same workspace clears the flag."""
+    W = weights(64, 2048, 55, dev)
+    try:
+        hqq.hqq_debug_solver(step_budget=2)
+        for zero_bits in (16, 8):
+            print(f"tiny step budget, zero_bits={zero_bits}", flush=True)
+            out = run(W, 4, 64, zero_bits, check=False)
+            with pytest.raises(hqq.HQQError) as e:
+                hqq.hqq_batch_check([out["job"]], out["workspace"])
+            assert e.value.status == hqq.HQQ_ERR_DEVICE
+            assert "step budget" in str(e.value)
+    finally:
+        hqq.hqq_debug_solver()
+    job, ws = out["job"], out["workspace"]
+    hqq.hqq_quantize_batch([job], ws)                 # same outputs and workspace, default budget
+    hqq.hqq_batch_check([job], ws)
+    compare(O, W, out, 4, 64, 8, label="after the flag")
 
 
 def test_empty_tensor(dev):

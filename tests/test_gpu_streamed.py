@@ -92,6 +92,32 @@ def test_streamed_equals_in_memory_batch(dev):
                 assert torch.equal(a[k], b[k]), k
 
 
+def test_consecutive_streamed_calls_share_staging(O, dev):
+    """Two calls in a row on one staging buffer with a separate copy stream: the second
+    call's first copies must wait for the first call's last solves, which still read the
+    staging halves."""
+    staging_bytes = 2 * 160 * 1024
+    staging = torch.empty(staging_bytes, dtype=torch.uint8, device=dev)
+    cs = torch.cuda.Stream()
+    calls = [_host_jobs(dev, 900), _host_jobs(dev, 950)]
+    ws = torch.empty(max(max(hqq.hqq_streamed_workspace_bytes(j, staging_bytes)
+                             for _, _, j in calls), 256), dtype=torch.uint8, device=dev)
+    for host, outs, jobs in calls:
+        hqq.hqq_quantize_streamed(jobs, staging, ws, None, cs.cuda_stream)
+    torch.cuda.synchronize()
+    for n, (host, outs, jobs) in enumerate(calls):
+        for (axis, nbits, g, zb, rows, cols), (Wh, Wd), o in zip(SPECS, host, outs):
+            label = f"call {n} axis={axis} nbits={nbits} g={g} zb={zb}"
+            if axis == 0:
+                check_axis0(O, Wd, o, nbits, g, zb, label)
+                continue
+            ref = O.quantize(u16(Wd), g, nbits, zero_bits=zb)
+            assert np.array_equal(u8(o["packed"])[:ref["packed"].size], ref["packed"]), label
+            assert np.array_equal(u16(o["scale"]), ref["scale"]), label
+            zero = u16(o["zero"]) if zb == 16 else u8(o["zero"])
+            assert np.array_equal(zero, ref["zero"]), label
+
+
 def test_streamed_rejects_a_tensor_larger_than_half(dev):
     host, outs, jobs = _host_jobs(dev, 800)
     staging = torch.empty(2 * 4096, dtype=torch.uint8, device=dev)
