@@ -39,8 +39,8 @@
 //    slot for larger ones), so the pool can never block.
 //  * Work that is cheaper across lanes runs in batches of GB groups with KB lanes per group
 //    (EB weights per lane): INIT (a prefetched tile of GB groups: min/max, s, z0, exact
-//    sum x*s; the groups become ready), EXACT (binary64 decisions and shrink updates) and
-//    EPILOGUE (codes of the accepted zero, packing, scale and zero stores).
+//    sum x*s, the tile's scales stored; the groups become ready), EXACT (binary64 decisions
+//    and shrink updates) and EPILOGUE (codes of the accepted zero, packing, zero stores).
 //  * The next tile's weights are in flight in registers while the wave works.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -633,7 +633,6 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 });
             }
             if (bleader) {
-                gbl(J.scale)[gidx] = f2h(1.0f / s);
                 if (J.zero16) gbl(J.zero16)[gidx] = f2h(zb);
                 if (J.zero32) gbl(J.zero32)[gidx] = zb;
                 // evaluations run = index of the next update when the group stops
@@ -872,7 +871,10 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 continue;
             }
 
-            if (exq_n >= GB || (exq_n > 0 && idle && rdy_n == 0)) {
+            // A full batch, or whatever is pending once the wave is idle or has no tile left
+            // to claim: from then on a waiting group lengthens the wave's tail, so it should
+            // not wait for the other lanes' groups to finish first.
+            if (exq_n >= GB || (exq_n > 0 && (idle || !pf_ok) && rdy_n == 0)) {
                 // ================= EXACT: binary64 decisions and shrink updates ==============
                 __builtin_amdgcn_s_setprio(0);
                 const int n = exq_n < GB ? (int)exq_n : GB;
@@ -1067,6 +1069,9 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 sxs = fma((double)h2f(i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu), sd, sxs);
             sxs = addd_k<KB>(sxs);
             if (bleader) {
+                // The scale is fixed from here on: the tile's scales are stored now, one
+                // contiguous run per tile, rather than one by one as groups finish.
+                gbl(jobs[pf_job].scale)[pf_g0 + k] = f2h(1.0f / s);
                 st_a[j] = SlotA{s, z0, z0, 0.f};
                 float beta0 = a.beta0;
                 asm volatile("" : "+s"(beta0));     // kept in a scalar register until here
