@@ -392,6 +392,12 @@ size_t streamed_workspace(const hqq_job *jobs, const std::vector<Chunk> &chunks)
 
 }  // namespace
 
+int hqq::report_error(int status, const char *msg)
+{
+    g_last_error = msg;
+    return status;
+}
+
 extern "C" {
 
 size_t hqq_packed_bytes(int64_t n_codes, int nbits) { return packed_bytes(n_codes, nbits); }

@@ -40,6 +40,10 @@ struct StreamArgs {
     int64_t budget_tile;        // and what each tile it takes in adds
 };
 
+// Sets the calling thread's hqq_last_error() text and returns `status` (for entry points
+// defined outside hqq_api.hip).
+int report_error(int status, const char *msg);
+
 // Diagnostic settings of the solver launches. Step budget of the waves: 0 selects the
 // default (a bound the schedule never reaches); a positive value replaces the starting
 // budget and stops its growth per tile. Pass layout: 0 chosen by size, 1 wide, 2 narrow.

@@ -21,7 +21,7 @@ EXPORTS = ("hqq_packed_bytes", "hqq_workspace_bytes", "hqq_quantize", "hqq_quant
            "hqq_streamed_workspace_bytes", "hqq_dequantize", "hqq_gemm",
            "hqq_gemm_workspace_bytes", "hqq_gemm_f16", "hqq_requant_scales",
            "hqq_dequantize_scales", "hqq_pack", "hqq_unpack", "hqq_status_string",
-           "hqq_last_error", "hqq_batch_check", "hqq_debug_solver")
+           "hqq_last_error", "hqq_batch_check", "hqq_debug_solver", "hqq_quantize_noalloc")
 
 
 class HQQError(RuntimeError):
@@ -57,6 +57,9 @@ def lib():
         L.hqq_quantize.restype = i32
         L.hqq_quantize.argtypes = [vp, i64, i64, i32, i32, i32, f32, f32, f32, i32, i32, i32,
                                    vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.hqq_quantize_noalloc.restype = i32
+        L.hqq_quantize_noalloc.argtypes = [vp, i64, i64, i32, i32, i32, f32, f32, f32, i32, i32,
+                                           i32, vp, vp, vp, vp, vp, vp]
         for name in ("hqq_quantize_batch", "hqq_solve_batch", "hqq_requant_batch"):
             getattr(L, name).restype = i32
             getattr(L, name).argtypes = [C.POINTER(hqq_job), i32, vp, C.c_size_t, vp]
@@ -148,6 +151,16 @@ def hqq_quantize(W, nbits, group_size, axis, p, beta, kappa, iters, early_stop, 
                               iters, int(early_stop), zero_bits, _p(packed), _p(scale),
                               _p(zero), _p(zero_meta), _p(passes), _p(workspace), wsb,
                               _stream(stream)))
+
+
+def hqq_quantize_noalloc(W, nbits, group_size, axis, p, beta, kappa, iters, early_stop,
+                         zero_bits, packed, scale, zero, zero_meta, passes, stream=None) -> None:
+    """hqq_quantize on the library's static scratch (no workspace argument)."""
+    rows, cols = W.shape
+    _check(lib().hqq_quantize_noalloc(_p(W), rows, cols, nbits, group_size, axis, p, beta,
+                                      kappa, iters, int(early_stop), zero_bits, _p(packed),
+                                      _p(scale), _p(zero), _p(zero_meta), _p(passes),
+                                      _stream(stream)))
 
 
 def _batch(fn, jobs, workspace, stream):

@@ -109,6 +109,21 @@ hqq_status hqq_quantize(const void *W, int64_t rows, int64_t cols, int nbits, in
                         int zero_bits, void *packed, void *scale, void *zero, void *zero_meta,
                         uint8_t *passes, void *workspace, size_t workspace_bytes, void *stream);
 
+/* hqq_quantize without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and errors as hqq_quantize; it calls no hipMalloc, hipFree or
+ * allocating library routine. Its scratch is one static device array of 64 MiB that every
+ * GPU the library runs on holds until the process ends; the tensor's hqq_workspace_bytes()
+ * must fit it (every tensor of the model-shaped stacks at axis 1 does; axis 0 takes about
+ * 2 + nbits/8 bytes per weight), else HQQ_ERR_WORKSPACE and nothing is enqueued. All calls
+ * on one GPU share that array and the next call overwrites it: calls that overlap on one GPU
+ * (concurrent streams, or threads) race and must be ordered by the caller. */
+hqq_status hqq_quantize_noalloc(const void *W, int64_t rows, int64_t cols, int nbits,
+                                int group_size, int axis, float p, float beta, float kappa,
+                                int iters, int early_stop, int zero_bits, void *packed,
+                                void *scale, void *zero, void *zero_meta, uint8_t *passes,
+                                void *stream);
+
 /* Quantize several tensors with one launch sequence (e.g. every linear layer of a model
  * stack). `jobs` is a host array, read during the call only; every job is validated first.
  * Jobs may mix nbits and group sizes; each job's output is what hqq_quantize writes. */

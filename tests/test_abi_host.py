@@ -208,3 +208,17 @@ def test_gemm_validates(H):
     a = (X, 65, P, S, Z, None, 64, 128, 4, 64, 16, Y)
     assert gm(*a, ws=C.c_void_p(0x7000), wb=need - 1) == H.HQQ_ERR_WORKSPACE
     assert gm(*a, ws=C.c_void_p(0x7008), wb=need) == arg                # 16-byte alignment
+
+
+def test_noalloc_rejects_before_any_device_call(H):
+    """The no-workspace entry point validates like hqq_quantize and refuses a tensor whose
+    scratch would exceed its static 64 MiB, both before touching the device."""
+    L = H.lib()
+    args = [C.c_void_p(0x1000), 64, 256, 5, 64, 1, 0.7, 1.0, 1.01, 20, 1, 8,
+            C.c_void_p(0x2000), C.c_void_p(0x3000), C.c_void_p(0x4000), C.c_void_p(0x5000),
+            None, None]
+    assert L.hqq_quantize_noalloc(*args) == 1                      # nbits = 5
+    big = list(args)
+    big[1], big[2], big[3], big[5], big[11] = 8192, 8192, 4, 0, 16  # axis 0: ~156 MiB of scratch
+    assert L.hqq_quantize_noalloc(*big) == 3
+    assert "static scratch" in L.hqq_last_error().decode()
