@@ -171,7 +171,8 @@ void make_plan(const hqq_job *jobs, int n_jobs, char *ws, Plan &P)
                (j.passes ? round_up((size_t)ng) : 0);
     }
     const size_t off_mm = off;
-    off += round_up(sizeof(uint32_t) * 2 * (size_t)(n > 0 ? n : 1));
+    off += round_up(sizeof(uint32_t) * hqq::kMinmaxStride * hqq::kMinmaxSlots *
+                    (size_t)(n > 0 ? n : 1));
     P.off_table = off;
     off += round_up(sizeof(hqq::DevJob) * (size_t)(n > 0 ? n : 1));
     P.off_counters = off;                // one tile counter per class, then the status word
@@ -218,7 +219,8 @@ void make_plan(const hqq_job *jobs, int n_jobs, char *ws, Plan &P)
                 const bool t0 = j.axis == 0;
                 if (j.zero_bits == 8) {
                     d.zero32 = reinterpret_cast<float *>(ws + z_off[t]);
-                    d.minmax = reinterpret_cast<uint32_t *>(ws + off_mm) + 2 * t;
+                    d.minmax = reinterpret_cast<uint32_t *>(ws + off_mm) +
+                               hqq::kMinmaxStride * hqq::kMinmaxSlots * t;
                     d.zq = static_cast<uint8_t *>(t0 ? P.ax0.back().zero_t : j.zero);
                     d.meta = static_cast<uint16_t *>(j.zero_meta);
                 } else {

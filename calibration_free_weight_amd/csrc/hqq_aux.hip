@@ -35,7 +35,8 @@ __device__ __forceinline__ uint16_t f2h(float f)
 // over all zeros of the tensor, on the grid of its stored binary16 pair:
 //   step = binary16((zmax - zmin)/255) (1 if that is 0), base = binary16(zmin),
 //   zq = clamp(rne((z - base)/step), 0, 255), meta = {step, base}; read back zq*step + base.
-// The solver leaves each tensor's (zmin, zmax) as order-preserving integer keys.
+// The solver leaves each tensor's (zmin, zmax) as order-preserving integer keys, in
+// kMinmaxSlots copies that this kernel reduces once per job.
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ float unkey(uint32_t k)
 {
@@ -59,7 +60,9 @@ __global__ void __launch_bounds__(256) finish_kernel(const DevJob *table, int n_
         job_sh = lo;
     }
     __syncthreads();
-    int j = job_sh;
+    int j = job_sh, jc = -1;
+    uint16_t h_step = 0, h_base = 0;
+    float step = 1.0f, basef = 0.0f;
     for (int r = 0; r < kFinishPerThread; ++r) {
         const int64_t item = base + (int64_t)r * 256 + threadIdx.x;
         if (item >= n_items) break;
@@ -67,15 +70,24 @@ __global__ void __launch_bounds__(256) finish_kernel(const DevJob *table, int n_
         const DevJob &J = table[j];
         const int64_t i = item - J.item0;
         if (J.zq) {
-            const float zmin = unkey(J.minmax[0]), zmax = unkey(J.minmax[1]);
-            uint16_t h_step = f2h((zmax - zmin) / 255.0f);
-            float step = h2f(h_step);
-            if (!(step > 0.0f)) {
-                h_step = 0x3c00;                    // binary16 1.0
-                step = 1.0f;
+            if (j != jc) {                          // the tensor's grid, once per job
+                jc = j;
+                uint32_t kmin = 0xffffffffu, kmax = 0u;
+                for (int p = 0; p < kMinmaxSlots; ++p) {
+                    kmin = min(kmin, J.minmax[kMinmaxStride * p]);
+                    kmax = max(kmax, J.minmax[kMinmaxStride * p + 1]);
+                }
+                const float zmin = unkey(kmin), zmax = unkey(kmax);
+                h_step = f2h((zmax - zmin) / 255.0f);
+                step = h2f(h_step);
+                if (!(step > 0.0f)) {
+                    h_step = 0x3c00;                // binary16 1.0
+                    step = 1.0f;
+                }
+                h_base = f2h(zmin);
+                basef = h2f(h_base);
             }
-            const uint16_t h_base = f2h(zmin);
-            const float v = rintf((J.zero32[i] - h2f(h_base)) / step);
+            const float v = rintf((J.zero32[i] - basef) / step);
             J.zq[i] = (uint8_t)fminf(fmaxf(v, 0.0f), 255.0f);
             if (i == 0) {
                 J.meta[0] = h_step;

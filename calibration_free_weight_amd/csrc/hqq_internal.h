@@ -7,6 +7,11 @@
 namespace hqq {
 
 constexpr int kMaxIters = 254;      // passes are counted in uint8 (1..iters+1)
+// Copies of each tensor's (min, max) of the binary32 zeros: many small waves updating one
+// pair of words with atomics serialise on its cache line, so each wave takes the pair of its
+// slot, one slot per 128-byte line, and the requant kernel reduces the copies.
+constexpr int kMinmaxSlots = 64;
+constexpr int kMinmaxStride = 32;   // uint32 words between slots
 
 // One tensor as the device kernels see it (the job table lives in the caller's workspace).
 struct DevJob {
@@ -17,7 +22,9 @@ struct DevJob {
     float *zero32;              // binary32 zero staging for 8-bit zeros, or nullptr
     uint8_t *passes;            // nullable
     uint2 *stash;               // 3-bit: partial boundary words per group, or nullptr
-    uint32_t *minmax;           // 8-bit zeros: order-preserving keys {min, max}
+    uint32_t *minmax;           // 8-bit zeros: kMinmaxSlots pairs of order-preserving keys
+                                // {min, max}, kMinmaxStride words apart; a wave updates the
+                                // pair of its slot
     uint8_t *zq;                // 8-bit zeros out
     uint16_t *meta;             // 8-bit zeros: binary16 {step, base} out
     int64_t n_groups;

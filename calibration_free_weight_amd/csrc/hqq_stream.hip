@@ -527,8 +527,9 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
         if (mm_job >= 0) {
             const float lo = minf_k<64>(mm_lo), hi = maxf_k<64>(mm_hi);
             if (lane == 0) {
-                atomic_min_g(jobs[mm_job].minmax, fkey(lo));
-                atomic_max_g(jobs[mm_job].minmax + 1, fkey(hi));
+                uint32_t *mm = jobs[mm_job].minmax + kMinmaxStride * (blockIdx.x % kMinmaxSlots);
+                atomic_min_g(mm, fkey(lo));
+                atomic_max_g(mm + 1, fkey(hi));
             }
         }
         mm_lo = INFINITY;
@@ -1088,6 +1089,339 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
         __hip_atomic_fetch_or(gbl(a.status), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Exact (binary64) evaluation of a lane's EB weights held in registers at zero z (the
+// lockstep kernel's form of eval_exact).
+template <class C>
+__device__ __forceinline__ Exact eval_exact_regs(const uint32_t (&xb)[C::WB], float s, float z)
+{
+    const double sd = s, zd = z, qm = C::QMAX;
+    double s_ = 0.0, q_ = 0.0, d_ = 0.0;
+#pragma unroll 1
+    for (int i = 0; i < C::EB; ++i) {
+        const uint32_t h = i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu;
+        const double u = fma((double)h2f(h), sd, zd);
+        const double c = fmin(fmax(rint(u), 0.0), qm);
+        const double e = fabs(u - c);
+        s_ += e;
+        q_ += c;
+        d_ = fmax(d_, e);
+    }
+    return Exact{s_, q_, d_};
+}
+
+// Lockstep solver for classes too small to keep the persistent waves busy (a single layer,
+// say). One wave per tile of GB groups in the batch layout (KB lanes per group, EB weights
+// per lane, held in registers): every group of the tile is iterated in place, each loop turn
+// taking one step of each unfinished group -- a binary32 evaluation, an exact (binary64)
+// decision, or a zero update with a live shrink -- until all are done, then packed and
+// stored. No staging slots, rings or swaps: lanes whose group finished early idle, which
+// costs less than the persistent scheduler's latency when each wave has only a few tiles.
+// Every decision is the persistent kernel's, so the results are identical.
+enum : uint8_t { kStepFast = 0, kStepExact = 1, kStepShrink = 2, kStepDone = 3 };
+
+template <int NBITS, int G>
+__global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
+{
+    using C = Cfg<NBITS, G>;
+    constexpr int EB = C::EB, KB = C::KB, GB = C::GB, WB = C::WB;
+    __shared__ __attribute__((aligned(4))) uint8_t stage[NBITS == 3 ? 64 * EB : 4];
+    const int lane = threadIdx.x;
+    const int k = lane / KB, sub = lane % KB;
+    const bool bleader = sub == 0;
+    const int64_t tile = blockIdx.x;
+    // the tile's job (jobs ordered by tile0; wave-uniform search)
+    int lo = 0, hi = a.n_jobs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (jobs[mid].tile0 <= tile) lo = mid;
+        else hi = mid - 1;
+    }
+    const DevJob &J = jobs[(int)uniform((uint32_t)lo)];
+    const int64_t g0 = (tile - J.tile0) * GB;
+    const int64_t left = J.n_groups - g0;
+    const int nv = (int)(left < GB ? left : GB);
+    const bool valid = k < nv;
+    const int64_t gidx = g0 + (valid ? k : 0);      // lanes past a ragged end re-read group g0
+    uint32_t xb[WB];
+    {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(J.W + gidx * G + sub * EB);
+#pragma unroll
+        for (int i = 0; i < EB / 8; ++i) {
+            const u32x4 v = gbl(const_cast<u32x4 *>(src))[i];
+            xb[4 * i] = v.x;
+            xb[4 * i + 1] = v.y;
+            xb[4 * i + 2] = v.z;
+            xb[4 * i + 3] = v.w;
+        }
+    }
+    // Dead zone of the shrink (as in the persistent kernel).
+    const double tau_exp = -1.0 / (2.0 - (double)a.p);
+    float beta_last = a.beta0;
+    for (int i = 1; i < a.iters; ++i) beta_last = beta_last * a.kappa;
+    const float tau_min = __builtin_bit_cast(
+        float, uniform(__float_as_uint(
+                   a.iters > 0 ? (float)pow_ool((double)beta_last, tau_exp) * (1.0f - 4e-6f) : 0.0f)));
+    const double pm1 = (double)a.p - 1.0;
+
+    // ---- INIT: min / max on binary16 pairs, s, z0, exact sum x*s ----
+    h2v hmn = __builtin_bit_cast(h2v, xb[0]), hmx = hmn;
+#pragma unroll
+    for (int i = 1; i < WB; ++i) {
+        const h2v h = __builtin_bit_cast(h2v, xb[i]);
+        hmn = __builtin_elementwise_min(hmn, h);
+        hmx = __builtin_elementwise_max(hmx, h);
+    }
+    float mn = fminf((float)hmn.x, (float)hmn.y);
+    float mx = fmaxf((float)hmx.x, (float)hmx.y);
+    mn = minf_k<KB>(mn);
+    mx = maxf_k<KB>(mx);
+    const float rng = mx - mn;
+    const float s = rng > 0.0f ? C::QMAX / rng : 1.0f;
+    const double sd = s;
+    double X = 0.0;
+#pragma unroll
+    for (int i = 0; i < EB; ++i)
+        X = fma((double)h2f(i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu), sd, X);
+    X = addd_k<KB>(X);
+    if (valid && bleader) gbl(J.scale)[gidx] = f2h(1.0f / s);
+    // binary32 range test of the fast path: u of the extreme weights stays in range
+    const float umn = mn, umx = mx;
+
+    float z = 0.0f - mn * s, zb = z, Db = 0.0f, beta = a.beta0;
+    double Sb = 0.0;
+    int t = 1;
+    bool first = true, sbexact = false;
+    uint8_t step = valid ? kStepFast : kStepDone;
+    int64_t budget = a.budget0 + a.budget_tile;
+    bool ran_out = false;
+
+    while (__ballot(step != kStepDone)) {
+        if (--budget <= 0) {
+            ran_out = true;
+            break;
+        }
+        if (step == kStepFast) {
+            const float ulo = fmaf(umn, s, z), uhi = fmaf(umx, s, z);
+            if (!(ulo >= -0.5f && uhi < C::QMAX + 0.5f)) step = kStepExact;   // may clamp
+        }
+        // ---- binary32 evaluation ----
+        if (step == kStepFast) {
+            float S, T, D;
+            eval_fast<NBITS, WB>(xb, s, z, S, T, D);
+            if (KB > 1) {
+                S = addf_k<KB>(S);
+                T = addf_k<KB>(T);
+                D = maxf_k<KB>(D);
+            }
+            const float Q = (float)rint(fma((double)G, (double)z, X) - (double)T);
+            bool accept = false;
+            if (D >= C::kThr) {
+                step = kStepExact;
+            } else if (first || !a.early_stop) {
+                accept = true;
+            } else {
+                const float Sb32 = (float)Sb;
+                const float m = (float)C::kElemErr + S * 0x1p-18f +
+                                (sbexact ? 0x1p-18f * Sb32 : 4.0f * (float)C::kElemErr + Sb32 * 0x1p-18f);
+                if (S > Sb32 + m) step = kStepDone;
+                else if (S < Sb32 - m) accept = true;
+                else {
+                    first = false;
+                    step = kStepExact;
+                }
+            }
+            if (accept) {
+                zb = z;
+                Sb = S;
+                Db = D;
+                first = false;
+                sbexact = false;
+                const Advance ad = advance_core<C>(t, a.iters, s, z, Q, D, false, X, beta,
+                                                   tau_min, tau_exp);
+                if (ad.out == kDone) {
+                    zb = ad.zn;
+                    step = kStepDone;
+                } else if (ad.out == kNeedShrink) {
+                    step = kStepShrink;
+                } else {
+                    z = ad.zn;
+                    beta = beta * a.kappa;
+                    ++t;
+                }
+            }
+        }
+        // ---- exact decision (binary64), for the groups the fast path could not settle ----
+        if (__ballot(step == kStepExact)) {
+            if (step == kStepExact) {
+                const Exact xn = eval_exact_regs<C>(xb, s, z);
+                const double S = addd_k<KB>(xn.S);
+                const float Q = (float)addd_k<KB>(xn.Q);
+                const float D = maxf_k<KB>((float)xn.D);
+                double Sbx = Sb;
+                if (!first && !sbexact) Sbx = addd_k<KB>(eval_exact_regs<C>(xb, s, zb).S);
+                if (first || !a.early_stop || S <= Sbx) {
+                    zb = z;
+                    Db = D;
+                    Sb = S;
+                    first = false;
+                    sbexact = true;
+                    const Advance ad = advance_core<C>(t, a.iters, s, z, Q, D, true, X, beta,
+                                                       tau_min, tau_exp);
+                    if (ad.out == kDone) {
+                        zb = ad.zn;
+                        step = kStepDone;
+                    } else if (ad.out == kNeedShrink) {
+                        step = kStepShrink;
+                    } else {
+                        z = ad.zn;
+                        beta = beta * a.kappa;
+                        ++t;
+                        step = kStepFast;
+                    }
+                } else {
+                    step = kStepDone;
+                }
+            }
+        }
+        // ---- zero update with the shrink live: z = mean(q - (x - W_e)*s), W_e from the
+        //      residual r = x - W_r = (u - q)/s of the accepted iterate ----
+        if (__ballot(step == kStepShrink)) {
+            if (step == kStepShrink) {
+                const double zd = zb, qm = C::QMAX, bd = beta;
+                double acc = 0.0;
+#pragma unroll 1
+                for (int i = 0; i < EB; ++i) {
+                    const double xv = h2f(i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu);
+                    const double u = fma(xv, sd, zd);
+                    const double c = fmin(fmax(rint(u), 0.0), qm);
+                    const double we = shrink((u - c) / sd, pm1, bd);
+                    acc += c - (xv - we) * sd;
+                }
+                acc = addd_k<KB>(acc);
+                z = (float)(acc * (1.0 / G));
+                beta = (float)bd * a.kappa;
+                ++t;
+                first = false;
+                step = kStepFast;
+            }
+        }
+    }
+
+    // ---- EPILOGUE: codes of the accepted zero, packed; zero and count stores ----
+    const int64_t e0 = gidx * G + sub * EB;
+    auto emit = [&](auto val) {
+        constexpr int PL = NBITS == 3 ? 1 : 8 / NBITS;   // planes
+        constexpr int BY = EB / PL < 4 ? EB / PL : 4;    // bytes per word
+        constexpr int PER = BY * PL;                     // codes per word
+        constexpr int NW = EB / PER;
+        uint32_t pl[NW][PL];
+#pragma unroll
+        for (int q = 0; q < NW; ++q)
+#pragma unroll
+            for (int m = 0; m < PL; ++m) pl[q][m] = 0u;
+#pragma unroll
+        for (int i = 0; i < EB; ++i) {
+            const uint32_t h = i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu;
+            const int q = i / PER, m = i % PL, b = (i % PER) / PL;
+            pl[q][m] = __builtin_amdgcn_cvt_pk_u8_f32(val(h), b, pl[q][m]);
+        }
+        uint32_t w[NW];
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+            uint32_t word = pl[q][0];
+#pragma unroll
+            for (int m = 1; m < PL; ++m) word |= pl[q][m] << (NBITS * m);
+            w[q] = word;
+        }
+        if constexpr (NBITS == 3) {
+#pragma unroll
+            for (int q = 0; q < NW; ++q) *reinterpret_cast<uint32_t *>(stage + lane * EB + 4 * q) = w[q];
+        } else if (valid) {
+            uint8_t *dst = J.packed + e0 * NBITS / 8;
+            if constexpr (BY == 2)
+                *gbl(reinterpret_cast<uint16_t *>(dst)) = (uint16_t)w[0];
+            else if constexpr (NW == 4)
+                *gbl(reinterpret_cast<u32x4 *>(dst)) = u32x4{w[0], w[1], w[2], w[3]};
+            else if constexpr (NW == 2)
+                *gbl(reinterpret_cast<u32x2 *>(dst)) = u32x2{w[0], w[1]};
+            else if constexpr (NW == 1)
+                *gbl(reinterpret_cast<uint32_t *>(dst)) = w[0];
+            else {
+#pragma unroll
+                for (int q = 0; q < NW / 4; ++q)
+                    gbl(reinterpret_cast<u32x4 *>(dst))[q] =
+                        u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+            }
+        }
+    };
+    // the accepted evaluation's D bounds these codes (as in the persistent kernel's epilogue)
+    if (Db < C::kThr - (float)(1.0 / (1 << (24 - NBITS)))) {
+        emit([&](uint32_t h) { return fmaf(h2f(h), s, zb); });
+    } else {
+        emit([&](uint32_t h) {
+            // the empty asm keeps the compiler from reusing INIT's binary64 conversions of
+            // the weights here, which would keep all of them live through the loop
+            asm volatile("" : "+v"(h));
+            const double u = fma((double)h2f(h), (double)s, (double)zb);
+            return (float)fmin(fmax(rint(u), 0.0), (double)C::QMAX);
+        });
+    }
+    if constexpr (NBITS == 3) {
+        // flat 10-code words wholly inside a group are written here; a word shared with a
+        // neighbouring group goes to the stash (joined after the solve)
+        __syncthreads();
+        if (valid) {
+            const int64_t c0 = gidx * G, c1 = c0 + G, ncode = J.n_groups * G;
+            const int64_t w0 = c0 / 10, w1 = (c1 - 1) / 10;
+            auto out = gbl(reinterpret_cast<uint32_t *>(J.packed));
+            for (int64_t w = w0 + sub; w <= w1; w += KB) {
+                uint32_t word = 0;
+#pragma unroll
+                for (int c = 0; c < 10; ++c) {
+                    const int64_t ci = w * 10 + c;
+                    if (ci >= c0 && ci < c1) word |= (uint32_t)stage[k * G + (int)(ci - c0)] << (3 * c);
+                }
+                const bool head = w * 10 < c0;
+                const bool tail = w * 10 + 10 > c1 && c1 < ncode;
+                uint32_t *st2 = reinterpret_cast<uint32_t *>(J.stash + gidx);
+                if (head) gbl(st2)[1] = word;
+                else if (tail) gbl(st2)[0] = word;
+                else out[w] = word;
+            }
+        }
+    }
+    if (valid && bleader) {
+        if (J.zero16) gbl(J.zero16)[gidx] = f2h(zb);
+        if (J.zero32) gbl(J.zero32)[gidx] = zb;
+        if (J.passes) gbl(J.passes)[gidx] = (uint8_t)t;
+    }
+    if (J.minmax) {                          // the tensor's (min, max) of the binary32 zeros
+        const float lo_z = minf_k<64>(valid ? zb : INFINITY);
+        const float hi_z = maxf_k<64>(valid ? zb : -INFINITY);
+        if (lane == 0) {
+            uint32_t *mm = J.minmax + kMinmaxStride * (blockIdx.x % kMinmaxSlots);
+            atomic_min_g(mm, fkey(lo_z));
+            atomic_max_g(mm + 1, fkey(hi_z));
+        }
+    }
+    if (ran_out && lane == 0)
+        __hip_atomic_fetch_or(gbl(a.status), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int NBITS, int G>
+hipError_t launch_lockstep(StreamArgs a, hipStream_t stream)
+{
+    using C = Cfg<NBITS, G>;
+    const int64_t fixed = step_budget();
+    // every loop turn advances at least one group by one step; a group takes at most
+    // 2*(iters + 1) evaluations and updates plus its exact decisions
+    a.budget0 = fixed > 0 ? fixed : 8 * (int64_t)(a.iters + 4) * C::GB;
+    a.budget_tile = 0;
+    hipLaunchKernelGGL((lockstep_kernel<NBITS, G>), dim3((unsigned)a.n_tiles), dim3(64), 0,
+                       stream, a, a.jobs);
+    return hipGetLastError();
+}
+
 template <int NBITS, int G, int EPL>
 hipError_t launch_layout(StreamArgs a, int cus, hipStream_t stream)
 {
@@ -1122,17 +1456,15 @@ hipError_t launch_one(const StreamArgs &a, hipStream_t stream)
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
             cus = v;
     }
-    if constexpr (narrow_ep<G>() == wide_ep<G>()) {
-        return launch_layout<NBITS, G, wide_ep<G>()>(a, cus, stream);
-    } else {
-        // Narrow when the class's groups would give each lane of the machine fewer than
-        // about four (the wide layout holds up to 12 waves of 64 groups per compute unit).
-        const int64_t groups = a.n_tiles * Cfg<NBITS, G>::GB;
-        const int mode = solver_layout();
-        const bool narrow = mode == 2 || (mode == 0 && groups < 4 * (int64_t)cus * 12 * 64);
-        if (narrow) return launch_layout<NBITS, G, narrow_ep<G>()>(a, cus, stream);
-        return launch_layout<NBITS, G, wide_ep<G>()>(a, cus, stream);
-    }
+    // Lockstep when the class's groups would give each lane of the persistent grid (up to 12
+    // waves of 64 lanes per compute unit) fewer than about four; else the persistent solver.
+    const int64_t groups = a.n_tiles * Cfg<NBITS, G>::GB;
+    const int mode = solver_layout();
+    if (mode == 3 || (mode == 0 && groups < 4 * (int64_t)cus * 12 * 64))
+        return launch_lockstep<NBITS, G>(a, stream);
+    if constexpr (narrow_ep<G>() != wide_ep<G>())
+        if (mode == 2) return launch_layout<NBITS, G, narrow_ep<G>()>(a, cus, stream);
+    return launch_layout<NBITS, G, wide_ep<G>()>(a, cus, stream);
 }
 
 template <int NBITS>
@@ -1155,8 +1487,10 @@ __global__ void fill_kernel(FillArgs f, DevJob *table)
         const DevJob j = f.jobs[i];
         table[f.offset + i] = j;
         if (j.minmax) {
-            j.minmax[0] = 0xffffffffu;
-            j.minmax[1] = 0u;
+            for (int p = 0; p < kMinmaxSlots; ++p) {
+                j.minmax[kMinmaxStride * p] = 0xffffffffu;
+                j.minmax[kMinmaxStride * p + 1] = 0u;
+            }
         }
     }
     if (f.offset == 0)
@@ -1171,7 +1505,7 @@ std::atomic<int> g_layout{0};
 void set_solver_debug(int64_t steps, int layout)
 {
     g_step_budget.store(steps > 0 ? steps : 0);
-    g_layout.store(layout == 1 || layout == 2 ? layout : 0);
+    g_layout.store(layout >= 1 && layout <= 3 ? layout : 0);
 }
 int64_t step_budget() { return g_step_budget.load(); }
 int solver_layout() { return g_layout.load(); }

@@ -188,8 +188,9 @@ def hqq_batch_check(jobs, workspace, stream=None) -> None:
 
 
 def hqq_debug_solver(step_budget: int = 0, pass_layout: int = 0) -> None:
-    """Test hook: a fixed solver step budget (0 = default) and the pass layout (0 = by
-    size, 1 = one lane per group, 2 = several lanes per group)."""
+    """Test hook: a fixed solver step budget (0 = default) and the solver kernel (0 = by
+    size, 1 = persistent with one lane per group, 2 = persistent with several lanes per
+    group, 3 = lockstep)."""
     lib().hqq_debug_solver(int(step_budget), int(pass_layout))
 
 

@@ -157,10 +157,11 @@ hqq_status hqq_batch_check(const hqq_job *jobs, int n_jobs, const void *workspac
 /* Diagnostic hook for tests; the settings apply to every solver launch made afterwards, by
  * any thread. step_budget > 0 gives each solver wave a fixed budget of that many loop steps
  * (0 restores the default): with a small budget the solver ends early, every wave still
- * exits normally, and hqq_batch_check reports the incomplete batch. pass_layout selects how
- * lanes share a group during the solver's passes: 0 by the size of the batch (the default),
- * 1 one lane per group (wide), 2 several lanes per group (narrow, the layout for small
- * tensors); results are identical, only the speed differs. */
+ * exits normally, and hqq_batch_check reports the incomplete batch. pass_layout selects the
+ * solver kernel: 0 by the size of the batch (the default), 1 the persistent solver with one
+ * lane per group (wide), 2 the persistent solver with several lanes per group (narrow), 3 the
+ * lockstep solver (one wave per tile; the default for small batches); results are identical,
+ * only the speed differs. */
 void hqq_debug_solver(int64_t step_budget, int pass_layout);
 
 /* Quantize a batch whose weights live in HOST memory, for stacks larger than the device

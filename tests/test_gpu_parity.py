@@ -66,12 +66,13 @@ def test_quantize_matches_oracle(O, dev, nbits, g, zero_bits):
     compare(O, W, out, nbits, g, zero_bits, label=f"b{nbits} g{g} z{zero_bits}")
 
 
-@pytest.mark.parametrize("layout", [1, 2], ids=["wide", "narrow"])
+@pytest.mark.parametrize("layout", [1, 2, 3], ids=["wide", "narrow", "lockstep"])
 @pytest.mark.parametrize("nbits", [1, 2, 3, 4, 8])
 def test_both_pass_layouts(O, dev, nbits, layout):
-    """The solver's two pass layouts (one lane per group; several lanes per group, chosen for
-    small tensors) give identical results: forced here for every bit width and group size,
-    on boundary groups that exercise the exact path and with a live shrink."""
+    """The solver's kernels (persistent with one lane per group or several lanes per group;
+    lockstep, chosen for small batches) give identical results: forced here for every bit
+    width and group size, on boundary groups that exercise the exact path, with 8-bit zeros
+    and with a live shrink."""
     try:
         hqq.hqq_debug_solver(pass_layout=layout)
         for g in (16, 32, 64, 128, 256):
@@ -182,14 +183,15 @@ def test_step_budget_exhaustion_is_reported(O, dev):
     the next solve on the same workspace clears the flag."""
     W = weights(64, 2048, 55, dev)
     try:
-        hqq.hqq_debug_solver(step_budget=2)
-        for zero_bits in (16, 8):
-            print(f"tiny step budget, zero_bits={zero_bits}", flush=True)
-            out = run(W, 4, 64, zero_bits, check=False)
-            with pytest.raises(hqq.HQQError) as e:
-                hqq.hqq_batch_check([out["job"]], out["workspace"])
-            assert e.value.status == hqq.HQQ_ERR_DEVICE
-            assert "step budget" in str(e.value)
+        for layout in (1, 3):                     # persistent and lockstep solvers
+            hqq.hqq_debug_solver(step_budget=2, pass_layout=layout)
+            for zero_bits in (16, 8):
+                print(f"tiny step budget, layout={layout} zero_bits={zero_bits}", flush=True)
+                out = run(W, 4, 64, zero_bits, check=False)
+                with pytest.raises(hqq.HQQError) as e:
+                    hqq.hqq_batch_check([out["job"]], out["workspace"])
+                assert e.value.status == hqq.HQQ_ERR_DEVICE
+                assert "step budget" in str(e.value)
     finally:
         hqq.hqq_debug_solver()
     job, ws = out["job"], out["workspace"]
