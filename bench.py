@@ -2,11 +2,13 @@
 """Throughput of the HQQ quantizer on one MI355X.
 
 A step quantizes one whole Llama-2-7B-shaped stack (32 blocks x q,k,v,o,gate,up,down,
-224 tensors, 6.48e9 binary16 weights resident in HBM; 4-bit, group 64... see --workload)
-through the C ABI: the group solver over every tensor, then the per-tensor 8-bit zero
-requantization. Prints one JSON line.
+224 tensors, 6.48e9 binary16 weights resident in HBM; 4-bit, group 128, 8-bit zeros; see
+--workload for the others) through the C ABI: the group solver over every tensor, then the
+per-tensor 8-bit zero requantization. Prints one JSON line; beside the main line it measures
+the other workloads, the stress input (beta0 = 1e4), the variants the pages describe and
+the oracle on the host.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--oracle-all-core]
 """
 from __future__ import annotations
 
@@ -87,14 +89,12 @@ def copy_probe(mib: int, dev):
     del a, b
 
 
-def cpu_baseline(specs, weights, seconds):
+def cpu_baseline(block0, seconds):
     """The oracle, single-threaded, on a bounded sample of the same weights: leading rows of
-    each distinct projection of block 0, grown until about `seconds` of CPU work."""
-    import numpy as np
+    each distinct projection of block 0 (host copies), sized to about `seconds` of CPU work."""
     import oracle
     from synth import half_bits
     O = oracle.Oracle()
-    block0 = [(s, w) for s, w in zip(specs, weights) if s.block == 0]
     # calibrate on a small slice, then size the sample
     s0, w0 = block0[0]
     probe_rows = max(1, 65536 // s0.cols)
@@ -105,7 +105,7 @@ def cpu_baseline(specs, weights, seconds):
     per_tensor = rate * seconds / len(block0)
     total_w, total_t, parts = 0, 0.0, []
     for s, w in block0:
-        rows = int(max(1, min(s.rows, per_tensor // s.cols)))
+        rows = int(max(1, min(w.shape[0], per_tensor // s.cols)))
         x = half_bits(w[:rows]).reshape(-1)
         t = time.perf_counter()
         O.quantize(x, s.group_size, s.nbits, zero_bits=s.zero_bits)
@@ -404,6 +404,171 @@ def gemm_row(specs, outs, dev, stream, reps=5):
     return res
 
 
+def build_workload(number, dev, beta=1.0, sets=1):
+    """Weights of a workload resident in HBM, preallocated outputs and a workspace. With
+    sets > 1 (the single-matrix workload, which fits the 256 MB last-level cache) that many
+    input/output sets are made so that consecutive launches stream from HBM."""
+    import synth
+    from calibration_free_weight_amd import hqq
+    specs = synth.workload(number)
+    weights, outs, job_sets, keep = [], [], [], []
+    for r in range(sets):
+        js = []
+        for s in specs:
+            seed = s.seed(number) + 7919 * r
+            w = synth.student_t_weights(s.rows, s.cols, seed, device=dev)
+            o = hqq.alloc_outputs(s.rows, s.cols, s.nbits, s.group_size, s.zero_bits, dev)
+            js.append(hqq.make_job(w, s.nbits, s.group_size, 1, 0.7, beta, 1.01, 20, 1,
+                                   s.zero_bits, o["packed"], o["scale"], o["zero"],
+                                   o["zero_meta"]))
+            if r == 0:
+                weights.append(w)
+                outs.append(o)
+            else:
+                keep.append((w, o))
+        job_sets.append(js)
+    ws = hqq.alloc_workspace(job_sets[0], dev)
+    return dict(specs=specs, weights=weights, outs=outs, job_sets=job_sets, ws=ws, keep=keep)
+
+
+def time_steps(wl, stream, steps, warmup):
+    """Runs `steps` steps (solve, then requant) after `warmup` untimed ones, rotating over the
+    workload's sets. Returns the wall seconds of the timed steps and the per-step solver and
+    requant times in ms from HIP events on the launch stream."""
+    import torch
+    from calibration_free_weight_amd import hqq
+    js_all, ws = wl["job_sets"], wl["ws"]
+    for i in range(warmup):
+        hqq.hqq_quantize_batch(js_all[i % len(js_all)], ws, stream.cuda_stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        js = js_all[k % len(js_all)]
+        ev[k][0].record(stream)
+        hqq.hqq_solve_batch(js, ws, stream.cuda_stream)
+        ev[k][1].record(stream)
+        hqq.hqq_requant_batch(js, ws, stream.cuda_stream)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    hqq.hqq_batch_check(js_all[(steps - 1) % len(js_all)], ws, stream.cuda_stream)
+    solve = [e[0].elapsed_time(e[1]) for e in ev]
+    req = [e[1].elapsed_time(e[2]) for e in ev]
+    return wall, solve, req
+
+
+def mean_passes(wl, stream, dev):
+    """Mean evaluations per group, from the solver's own per-group counts: one more (untimed)
+    solve of the first set with the count outputs set."""
+    import torch
+    from calibration_free_weight_amd import hqq
+    counts = []
+    for s, j in zip(wl["specs"], wl["job_sets"][0]):
+        pb = torch.empty(s.numel // s.group_size, dtype=torch.uint8, device=dev)
+        j.passes = pb.data_ptr()
+        counts.append(pb)
+    hqq.hqq_solve_batch(wl["job_sets"][0], wl["ws"], stream.cuda_stream)
+    torch.cuda.synchronize()
+    n_pass = sum(int(pb.sum(dtype=torch.int64).item()) for pb in counts)
+    n_groups = sum(pb.numel() for pb in counts)
+    for j in wl["job_sets"][0]:
+        j.passes = None
+    return n_pass / n_groups
+
+
+def roofline(specs, solve_ms, passes):
+    """Both roofs of the solver launches: algorithmic HBM bytes and algorithmic fp32 lane
+    operations per launch (one launch per class of tensors sharing bit width and group size)
+    over the median launch time; the binding roof is the one with the longer floor."""
+    classes = sorted({(s.nbits, s.group_size) for s in specs})
+    launches = len(classes)
+    n_weights = sum(s.numel for s in specs)
+    launch_s = solve_ms * 1e-3 / launches
+    bytes_launch = sum(alg_bytes(s) for s in specs) / launches
+    ops_launch = n_weights * alg_ops_per_weight(passes) / launches
+    hbm = {"achieved": round(bytes_launch / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "floor_ms": round(bytes_launch / HBM_PEAK_GBS / 1e6, 4)}
+    hbm["frac"] = round(hbm["achieved"] / HBM_PEAK_GBS, 4)
+    alu = {"achieved": round(ops_launch / launch_s / 1e12, 3), "peak": round(ALU_PEAK_TOPS, 3),
+           "unit": "Top/s", "floor_ms": round(ops_launch / ALU_PEAK_TOPS / 1e9, 4)}
+    alu["frac"] = round(alu["achieved"] / ALU_PEAK_TOPS, 4)
+    bound, main = ("alu", alu) if alu["floor_ms"] > hbm["floor_ms"] else ("hbm", hbm)
+    # The library runs a class on the lockstep kernel when it has fewer than about four groups
+    # per lane of the persistent grid (256 compute units x 12 waves x 64 lanes), else on the
+    # persistent one.
+    def kernel_name(b, g):
+        groups = sum(s.numel // s.group_size for s in specs if (s.nbits, s.group_size) == (b, g))
+        small = groups < 4 * 256 * 12 * 64
+        return f"{'lockstep_kernel' if small else 'stream_kernel'}<{b},{g}>"
+    return {"bound": bound,
+            "kernel": ", ".join(kernel_name(b, g) for b, g in classes),
+            "achieved": main["achieved"], "peak": main["peak"], "unit": main["unit"],
+            "frac": main["frac"], "launch_ms": round(launch_s * 1e3, 5),
+            "bytes_per_launch": round(bytes_launch, 1), "ops_per_launch": round(ops_launch, 1),
+            "mean_passes": round(passes, 4), "hbm": hbm, "alu": alu}
+
+
+def config_row(number, dev, stream, steps, beta=1.0, sets=1):
+    """One workload measured like the main line: seconds per stack (median over the steps of
+    solve + requant, HIP events), binary16 GB/s quantized, and the solver's roofs."""
+    import statistics
+    import synth
+    wl = build_workload(number, dev, beta=beta, sets=sets)
+    _, solve, req = time_steps(wl, stream, steps, warmup=2)
+    passes = mean_passes(wl, stream, dev)
+    n = sum(s.numel for s in wl["specs"])
+    step_ms = statistics.median(a + b for a, b in zip(solve, req))
+    row = {"workload": synth.WORKLOAD_NAMES[number], "beta": beta, "weights": n,
+           "steps": steps, "sets": sets, "ms_per_stack": round(step_ms, 4),
+           "value_gbs": round(2.0 * n / (step_ms * 1e-3) / 1e9, 1),
+           "solve_ms_median": round(statistics.median(solve), 4),
+           "requant_ms_median": round(statistics.median(req), 4),
+           "pct_hbm_peak": round(100.0 * sum(alg_bytes(s) for s in wl["specs"]) /
+                                 (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+           "roofline": roofline(wl["specs"], statistics.median(solve), passes)}
+    del wl
+    return row
+
+
+def oracle_all_core(wl, stream):
+    """The whole stack through the oracle on P single-threaded processes (one per host core,
+    at most 16), tensor by tensor, each result compared with what the GPU wrote. Reports the
+    wall time of the oracle with P stated."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle.pool import OraclePool
+    from calibration_free_weight_amd import hqq
+    O = oracle.Oracle()
+    hqq.hqq_quantize_batch(wl["job_sets"][0], wl["ws"], stream.cuda_stream)
+    torch.cuda.synchronize()
+    n_w, t_oracle, mismatches = 0, 0.0, 0
+    with OraclePool() as pool:
+        for s, w, o in zip(wl["specs"], wl["weights"], wl["outs"]):
+            w16 = w.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+            t = time.perf_counter()
+            ref = pool.solve_groups(w16.reshape(-1), s.group_size, s.nbits)
+            t_oracle += time.perf_counter() - t
+            n_w += s.numel
+            packed = o["packed"].cpu().numpy()
+            mismatches += int(not np.array_equal(packed[:O.packed_bytes(s.numel, s.nbits)],
+                                                 O.pack(ref["codes"], s.nbits)))
+            zq, meta = O.zero_requant(ref["zero_f32"])
+            mismatches += int(not np.array_equal(o["zero"].cpu().numpy(), zq))
+            mismatches += int(not np.array_equal(
+                o["scale"].cpu().view(torch.int16).numpy().view(np.uint16), ref["scale"]))
+            if s.proj == 6:
+                log(f"bench: oracle on block {s.block} done ({t_oracle:.0f} s)")
+        procs = pool.procs
+    return {"kind": "oracle", "procs": procs, "weights": n_w, "wall_s": round(t_oracle, 2),
+            "value": round(2.0 * n_w / t_oracle / 1e9, 5), "unit": "GB/s",
+            "tensors_differing": mismatches,
+            "note": "oracle (single-threaded C) in P processes over the tensor's groups; "
+                    "wall time of the solves only, host copies excluded"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,6 +579,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-next-rows", action="store_true",
                     help="only the main step (for a kernel trace of the solver alone)")
+    ap.add_argument("--oracle-all-core", action="store_true",
+                    help="also run the oracle over the whole workload on every host core "
+                         "(minutes) and compare it with the GPU")
+    ap.add_argument("--beta", type=float, default=1.0,
+                    help="beta0 of the main line (1e4 makes the shrink live: stress input)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -422,107 +592,44 @@ def main():
               "(the quantizer shards by whole tensors with no communication)", file=sys.stderr)
         sys.exit(2)
 
+    import statistics
     import torch
     import synth
-    from calibration_free_weight_amd import hqq
 
     dev = torch.device("cuda:0")
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, dev)
-    specs = synth.workload(args.workload)
-    n_weights = sum(s.numel for s in specs)
-    log(f"bench: workload {args.workload} ({synth.WORKLOAD_NAMES[args.workload]}), "
-        f"{len(specs)} tensors, {n_weights / 1e9:.3f}e9 weights")
-    # Inputs resident in HBM; outputs and workspace preallocated.
-    weights, outs, jobs = [], [], []
-    for s in specs:
-        w = synth.student_t_weights(s.rows, s.cols, s.seed(args.workload), device=dev)
-        o = hqq.alloc_outputs(s.rows, s.cols, s.nbits, s.group_size, s.zero_bits, dev)
-        jobs.append(hqq.make_job(w, s.nbits, s.group_size, 1, 0.7, 1.0, 1.01, 20, 1,
-                                 s.zero_bits, o["packed"], o["scale"], o["zero"],
-                                 o["zero_meta"]))
-        weights.append(w)
-        outs.append(o)
-    ws = hqq.alloc_workspace(jobs, dev)
-    # Config 1 fits the 256 MB last-level cache: rotate 16 input/output sets so every step
-    # streams from HBM.
-    job_sets = [jobs]
-    keep = []
-    if args.workload == 1:
-        for r in range(15):
-            s = specs[0]
-            w = synth.student_t_weights(s.rows, s.cols, s.seed(1) + 7919 * (r + 1), device=dev)
-            o = hqq.alloc_outputs(s.rows, s.cols, s.nbits, s.group_size, s.zero_bits, dev)
-            keep.append((w, o))
-            job_sets.append([hqq.make_job(w, s.nbits, s.group_size, 1, 0.7, 1.0, 1.01, 20, 1,
-                                          s.zero_bits, o["packed"], o["scale"], o["zero"],
-                                          o["zero_meta"])])
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    log("bench: inputs ready")
+    log(f"bench: workload {args.workload} ({synth.WORKLOAD_NAMES[args.workload]})")
+    # Inputs resident in HBM; outputs and workspace preallocated. The single-matrix workload
+    # rotates 16 sets (512 MiB of inputs) so that every step streams from HBM.
+    wl = build_workload(args.workload, dev, beta=args.beta,
+                        sets=16 if args.workload == 1 else 1)
+    specs, weights, outs = wl["specs"], wl["weights"], wl["outs"]
+    n_weights = sum(s.numel for s in specs)
+    log(f"bench: {len(specs)} tensors, {n_weights / 1e9:.3f}e9 weights ready")
+    cpu_input = None
+    if not args.no_cpu_baseline:             # host copy of the oracle's sample, taken now
+        cpu_input = [(s, w[:max(1, min(s.rows, 12_000_000 // s.cols))].cpu())
+                     for s, w in zip(specs, weights) if s.block == 0]
 
-    for i in range(args.warmup):
-        hqq.hqq_quantize_batch(job_sets[i % len(job_sets)], ws, stream.cuda_stream)
-    torch.cuda.synchronize()
-    log("bench: warmup done")
-
-    # Events on the stream the kernels run on: the solver phase of each step is bracketed.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        js = job_sets[k % len(job_sets)]
-        ev[k][0].record(stream)
-        hqq.hqq_solve_batch(js, ws, stream.cuda_stream)
-        ev[k][1].record(stream)
-        hqq.hqq_requant_batch(js, ws, stream.cuda_stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    steps = max(args.steps, 200) if args.workload == 1 else args.steps
+    wall, solve, req = time_steps(wl, stream, steps, args.warmup)
     log("bench: timed steps done")
-
-    # Mean evaluations per group, from the solver's own per-group counts: one more (untimed)
-    # solve of the whole batch with the count outputs set.
-    counts = []
-    for s, j in zip(specs, job_sets[0]):
-        pb = torch.empty(s.numel // s.group_size, dtype=torch.uint8, device=dev)
-        j.passes = pb.data_ptr()
-        counts.append(pb)
-    hqq.hqq_solve_batch(job_sets[0], ws, stream.cuda_stream)
-    torch.cuda.synchronize()
-    n_pass = sum(int(pb.sum(dtype=torch.int64).item()) for pb in counts)
-    n_groups = sum(pb.numel() for pb in counts)
-    mean_passes = n_pass / n_groups
-    for j in job_sets[0]:
-        j.passes = None
-    del counts
-
-    sec_per_step = (t1 - t0) / args.steps
+    passes = mean_passes(wl, stream, dev)
+    sec_per_step = wall / steps
     value = 2.0 * n_weights / sec_per_step / 1e9
-    solve_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
-    # One persistent solver launch per class of tensors sharing (nbits, group size).
-    classes = sorted({(s.nbits, s.group_size) for s in specs})
-    launches = len(classes)
-    kernel = ", ".join(f"stream_kernel<{b},{g}>" for b, g in classes)
+    solve_ms = statistics.median(solve)
     bytes_step = sum(alg_bytes(s) for s in specs)
-    launch_s = solve_ms * 1e-3 / launches
-    bytes_launch = bytes_step / launches
-    ops_launch = n_weights * alg_ops_per_weight(mean_passes) / launches
-    hbm = {"achieved": round(bytes_launch / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
-           "unit": "GB/s", "floor_ms": round(bytes_launch / HBM_PEAK_GBS / 1e6, 4)}
-    hbm["frac"] = round(hbm["achieved"] / HBM_PEAK_GBS, 4)
-    alu = {"achieved": round(ops_launch / launch_s / 1e12, 3), "peak": round(ALU_PEAK_TOPS, 3),
-           "unit": "Top/s", "floor_ms": round(ops_launch / ALU_PEAK_TOPS / 1e9, 4)}
-    alu["frac"] = round(alu["achieved"] / ALU_PEAK_TOPS, 4)
-    # The binding roof is the one with the longer floor.
-    bound, main = ("alu", alu) if alu["floor_ms"] > hbm["floor_ms"] else ("hbm", hbm)
-    traffic = measured_traffic(args.workload)
+    roof = roofline(specs, solve_ms, passes)
+    roof["launch_ms_mean"] = round(statistics.mean(solve) / len(roof["kernel"].split(", ")), 5)
+    roof["traffic"] = measured_traffic(args.workload)
     result = {
         "metric": METRIC,
         "value": round(value, 3),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(sec_per_step * 1e3, 4),
         "higher_is_better": True,
@@ -531,18 +638,13 @@ def main():
         "dtype": "f32+f64",
         "data": "synthetic",
         "config": {"workload": synth.WORKLOAD_NAMES[args.workload], "tensors": len(specs),
-                   "weights": n_weights, "p": 0.7, "beta": 1.0, "kappa": 1.01, "iters": 20,
-                   "early_stop": True},
+                   "weights": n_weights, "p": 0.7, "beta": args.beta, "kappa": 1.01,
+                   "iters": 20, "early_stop": True},
         "seconds_per_stack": round(sec_per_step, 6),
+        "seconds_per_stack_median_events": round(
+            statistics.median(a + b for a, b in zip(solve, req)) * 1e-3, 6),
         "pct_hbm_peak": round(100.0 * bytes_step / sec_per_step / 1e9 / HBM_PEAK_GBS, 3),
-        "roofline": {"bound": bound, "kernel": kernel, "achieved": main["achieved"],
-                     "peak": main["peak"], "unit": main["unit"], "frac": main["frac"],
-                     "traffic": traffic,
-                     "launch_ms": round(launch_s * 1e3, 5),
-                     "bytes_per_launch": round(bytes_launch, 1),
-                     "ops_per_launch": round(ops_launch, 1),
-                     "mean_passes": round(mean_passes, 4),
-                     "hbm": hbm, "alu": alu},
+        "roofline": roof,
     }
     if not args.skip_next_rows:
         log("bench: 8-bit scales")
@@ -556,9 +658,28 @@ def main():
         result["next_rows"]["gemm"] = gemm_row(specs, outs, dev, stream)
         log("bench: host streaming")
         result["next_rows"]["host_stream"] = host_stream_row(specs, weights, dev, stream)
-    if not args.no_cpu_baseline:
+    if args.oracle_all_core:
+        log("bench: the oracle over the whole workload on every host core")
+        result["oracle_all_core"] = oracle_all_core(wl, stream)
+        result["oracle_all_core"]["gpu_speedup"] = round(
+            result["oracle_all_core"]["wall_s"] / sec_per_step, 1)
+    del wl, specs, weights, outs
+    torch.cuda.empty_cache()
+    if args.workload == 2 and not args.skip_next_rows:
+        # the other workloads, each measured like the main line (config 1 over 16 rotating
+        # sets, 256 launches), and the stress input (config 1 with beta0 = 1e4: the shrink
+        # and its pow are live in most groups)
+        rows = {}
+        for number, steps_w, sets in ((1, 256, 16), (3, 5, 1), (4, 5, 1), (5, 3, 1)):
+            log(f"bench: workload {number}")
+            rows[f"workload{number}"] = config_row(number, dev, stream, steps_w, sets=sets)
+            torch.cuda.empty_cache()
+        log("bench: stress input")
+        rows["stress_beta1e4"] = config_row(1, dev, stream, 256, beta=1e4, sets=16)
+        result["next_rows"]["configs"] = rows
+    if cpu_input is not None:
         log("bench: timing the oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(specs, weights, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cpu_input, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

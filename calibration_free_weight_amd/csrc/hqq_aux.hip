@@ -45,10 +45,66 @@ __device__ __forceinline__ float unkey(uint32_t k)
 
 constexpr int kFinishPerThread = 8;
 
+// One job's view for the finish kernel, held in registers: the kernel's stores cannot then
+// force the job descriptor to be reloaded for every item.
+struct FinishJob {
+    const float *zero32;
+    uint8_t *zq;
+    uint16_t *meta;
+    const uint2 *stash;
+    uint32_t *packed;
+    int64_t item0, end;
+    uint32_t g;
+    uint16_t h_step, h_base;
+    float step, basef;
+};
+
+__device__ __forceinline__ FinishJob finish_job(const DevJob &J, int64_t end, uint32_t kmin,
+                                                uint32_t kmax)
+{
+    FinishJob f;
+    f.zero32 = J.zero32;
+    f.zq = J.zq;
+    f.meta = J.meta;
+    f.stash = J.stash;
+    f.packed = reinterpret_cast<uint32_t *>(J.packed);
+    f.item0 = J.item0;
+    f.end = end;
+    f.g = (uint32_t)J.g;
+    const float zmin = unkey(kmin), zmax = unkey(kmax);
+    f.h_step = f2h((zmax - zmin) / 255.0f);
+    f.step = h2f(f.h_step);
+    if (!(f.step > 0.0f)) {
+        f.h_step = 0x3c00;                          // binary16 1.0
+        f.step = 1.0f;
+    }
+    f.h_base = f2h(zmin);
+    f.basef = h2f(f.h_base);
+    return f;
+}
+
+__device__ __forceinline__ void finish_item(const FinishJob &f, int64_t item)
+{
+    const uint32_t i = (uint32_t)(item - f.item0);  // a group index (< 2^32 per tensor)
+    if (f.zq) {
+        const float v = rintf((f.zero32[i] - f.basef) / f.step);
+        f.zq[i] = (uint8_t)fminf(fmaxf(v, 0.0f), 255.0f);
+        if (i == 0) {
+            f.meta[0] = f.h_step;
+            f.meta[1] = f.h_base;
+        }
+    }
+    if (f.stash && i >= 1 && ((i % 10u) * (f.g % 10u)) % 10u != 0) {
+        const int64_t w = (int64_t)i * f.g / 10;
+        f.packed[w] = f.stash[i - 1].x | f.stash[i].y;
+    }
+}
+
 __global__ void __launch_bounds__(256) finish_kernel(const DevJob *table, int n_jobs,
                                                      int64_t n_items)
 {
     __shared__ int job_sh;
+    __shared__ uint32_t grid_sh[2];                 // job_sh's (min, max) keys, reduced
     const int64_t base = (int64_t)blockIdx.x * 256 * kFinishPerThread;
     if (threadIdx.x == 0) {
         int lo = 0, hi = n_jobs - 1;                // last job with item0 <= base
@@ -60,44 +116,46 @@ __global__ void __launch_bounds__(256) finish_kernel(const DevJob *table, int n_
         job_sh = lo;
     }
     __syncthreads();
-    int j = job_sh, jc = -1;
-    uint16_t h_step = 0, h_base = 0;
-    float step = 1.0f, basef = 0.0f;
+    const int j0 = job_sh;
+    // The first wave reduces the first job's key copies once for the block (one per lane).
+    if (threadIdx.x < 64) {
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+        if (table[j0].zq && threadIdx.x < kMinmaxSlots) {
+            kmin = table[j0].minmax[kMinmaxStride * threadIdx.x];
+            kmax = table[j0].minmax[kMinmaxStride * threadIdx.x + 1];
+        }
+        for (int d = 32; d >= 1; d >>= 1) {
+            kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
+            kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
+        }
+        if (threadIdx.x == 0) {
+            grid_sh[0] = kmin;
+            grid_sh[1] = kmax;
+        }
+    }
+    __syncthreads();
+    const FinishJob f0 =
+        finish_job(table[j0], j0 + 1 < n_jobs ? table[j0 + 1].item0 : n_items, grid_sh[0], grid_sh[1]);
+    int j = j0;
     for (int r = 0; r < kFinishPerThread; ++r) {
         const int64_t item = base + (int64_t)r * 256 + threadIdx.x;
         if (item >= n_items) break;
+        if (item < f0.end) {
+            finish_item(f0, item);
+            continue;
+        }
+        // a later job in this block (a block spans 2,048 items, a tensor far more): its
+        // descriptor and key copies straight from memory
         while (j + 1 < n_jobs && table[j + 1].item0 <= item) ++j;
-        const DevJob &J = table[j];
-        const int64_t i = item - J.item0;
-        if (J.zq) {
-            if (j != jc) {                          // the tensor's grid, once per job
-                jc = j;
-                uint32_t kmin = 0xffffffffu, kmax = 0u;
-                for (int p = 0; p < kMinmaxSlots; ++p) {
-                    kmin = min(kmin, J.minmax[kMinmaxStride * p]);
-                    kmax = max(kmax, J.minmax[kMinmaxStride * p + 1]);
-                }
-                const float zmin = unkey(kmin), zmax = unkey(kmax);
-                h_step = f2h((zmax - zmin) / 255.0f);
-                step = h2f(h_step);
-                if (!(step > 0.0f)) {
-                    h_step = 0x3c00;                // binary16 1.0
-                    step = 1.0f;
-                }
-                h_base = f2h(zmin);
-                basef = h2f(h_base);
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+        if (table[j].zq)
+            for (int p = 0; p < kMinmaxSlots; ++p) {
+                kmin = min(kmin, table[j].minmax[kMinmaxStride * p]);
+                kmax = max(kmax, table[j].minmax[kMinmaxStride * p + 1]);
             }
-            const float v = rintf((J.zero32[i] - basef) / step);
-            J.zq[i] = (uint8_t)fminf(fmaxf(v, 0.0f), 255.0f);
-            if (i == 0) {
-                J.meta[0] = h_step;
-                J.meta[1] = h_base;
-            }
-        }
-        if (J.stash && i >= 1 && (i * J.g) % 10 != 0) {
-            const int64_t w = i * J.g / 10;
-            reinterpret_cast<uint32_t *>(J.packed)[w] = J.stash[i - 1].x | J.stash[i].y;
-        }
+        const FinishJob fj =
+            finish_job(table[j], j + 1 < n_jobs ? table[j + 1].item0 : n_items, kmin, kmax);
+        finish_item(fj, item);
     }
 }
 
