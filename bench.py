@@ -292,7 +292,7 @@ def dequant_row(specs, outs, dev, stream, reps=5):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def gemm_row(specs, outs, dev, stream, reps=5):
+def gemm_row(specs, outs, dev, stream, reps=5, graphs=True):
     """The quantized linear layers of the stack (hqq_gemm on the 224 quantized weights the
     benchmark just wrote). Decode, M = 1, and small batches, M = 16 and 64 (the weight
     streams once per call): the 224 calls are captured in a HIP graph (launch gaps would
@@ -322,7 +322,7 @@ def gemm_row(specs, outs, dev, stream, reps=5):
         eager = [y.clone() for y in Ys]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         graphed = False
-        if m <= 64:
+        if m <= 64 and graphs:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 run_all()
@@ -579,6 +579,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-next-rows", action="store_true",
                     help="only the main step (for a kernel trace of the solver alone)")
+    ap.add_argument("--rows", default="scale8,axis0,dequant,gemm,host_stream,configs",
+                    help="which rows beside the main line to measure (comma-separated)")
+    ap.add_argument("--gemm-eager", action="store_true",
+                    help="launch the small-batch GEMM rows eagerly, not from HIP graphs (for "
+                         "counter passes)")
     ap.add_argument("--oracle-all-core", action="store_true",
                     help="also run the oracle over the whole workload on every host core "
                          "(minutes) and compare it with the GPU")
@@ -646,16 +651,22 @@ def main():
         "pct_hbm_peak": round(100.0 * bytes_step / sec_per_step / 1e9 / HBM_PEAK_GBS, 3),
         "roofline": roof,
     }
-    if not args.skip_next_rows:
+    want = set() if args.skip_next_rows else set(args.rows.split(","))
+    result["next_rows"] = {}
+    if "scale8" in want:
         log("bench: 8-bit scales")
-        result["next_rows"] = {"scale8": scale8_row(dev, stream)}
-    if args.workload == 2 and not args.skip_next_rows:
+        result["next_rows"]["scale8"] = scale8_row(dev, stream)
+    if args.workload == 2 and "axis0" in want:
         log("bench: axis 0")
         result["next_rows"]["axis0"] = axis0_row(specs, weights, dev, stream, solve_ms)
+    if args.workload == 2 and "dequant" in want:
         log("bench: dequantize")
         result["next_rows"]["dequant"] = dequant_row(specs, outs, dev, stream)
+    if args.workload == 2 and "gemm" in want:
         log("bench: quantized linear layers")
-        result["next_rows"]["gemm"] = gemm_row(specs, outs, dev, stream)
+        result["next_rows"]["gemm"] = gemm_row(specs, outs, dev, stream,
+                                               graphs=not args.gemm_eager)
+    if args.workload == 2 and "host_stream" in want:
         log("bench: host streaming")
         result["next_rows"]["host_stream"] = host_stream_row(specs, weights, dev, stream)
     if args.oracle_all_core:
@@ -665,7 +676,7 @@ def main():
             result["oracle_all_core"]["wall_s"] / sec_per_step, 1)
     del wl, specs, weights, outs
     torch.cuda.empty_cache()
-    if args.workload == 2 and not args.skip_next_rows:
+    if args.workload == 2 and "configs" in want:
         # the other workloads, each measured like the main line (config 1 over 16 rotating
         # sets, 256 launches), and the stress input (config 1 with beta0 = 1e4: the shrink
         # and its pow are live in most groups)
