@@ -35,8 +35,8 @@
 //    next-zero decision itself. No data moves between lanes and nothing touches memory.
 //  * A group that finishes, or whose decision needs the exact path, leaves its lane for a
 //    staging slot in LDS; the lane takes a ready group from LDS in its place. When both
-//    exist they exchange (in place with LDS atomic swaps for groups up to 64, through a spare
-//    slot for larger ones), so the pool can never block.
+//    exist they exchange (in place with LDS atomic swaps for a group held by one lane, through
+//    a spare slot for one spread over a lane pair), so the pool can never block.
 //  * Work that is cheaper across lanes runs in batches of GB groups with KB lanes per group
 //    (EB weights per lane): INIT (a prefetched tile of GB groups: min/max, s, z0, exact
 //    sum x*s, the tile's scales stored; the groups become ready), EXACT (binary64 decisions
@@ -57,7 +57,6 @@ enum : uint32_t { kEmpty = 0, kActive = 1, kHoldFin = 2, kHoldExq = 3 };   // a 
 // Group flags: bit 0 Sb/Db exact, bits 1-2 exact-path work, bit 3 first evaluation pending.
 enum : uint8_t { kSbExact = 1, kFirst = 8 };
 enum : uint8_t { kDecide = 1, kShrink = 2 };
-typedef _Float16 h2v __attribute__((ext_vector_type(2)));   // two binary16 weights
 
 // Global-address-space view of a pointer: global_* instructions count only against vmcnt,
 // whereas flat ones also hold lgkmcnt and would make LDS waits wait for memory.
@@ -118,6 +117,72 @@ HQQ_RED(float, dppf, minf)
 #undef HQQ_RED
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Packed binary16 min / max issued directly: through the builtins every loaded operand is first
+// quieted (a max of it with itself, one more instruction per pair), which changes only a
+// signalling NaN, and weights are finite by contract.
+__device__ __forceinline__ uint32_t pk_min_h(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ uint32_t pk_max_h(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// Min and max of a group's weights: a tree over the lane's binary16 pairs, then one packed
+// word {min, -max} reduced over the K lanes of the group (one packed min per step serves both).
+template <int W, int K>
+__device__ __forceinline__ void group_min_max(const uint32_t (&xb)[W], float &mn, float &mx)
+{
+    static_assert(W >= 2 && (W & (W - 1)) == 0, "pairs per lane: a power of two");
+    uint32_t lo[W / 2], hi[W / 2];
+#pragma unroll
+    for (int i = 0; i < W / 2; ++i) {
+        lo[i] = pk_min_h(xb[2 * i], xb[2 * i + 1]);
+        hi[i] = pk_max_h(xb[2 * i], xb[2 * i + 1]);
+    }
+#pragma unroll
+    for (int w = W / 4; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) {
+            lo[i] = pk_min_h(lo[2 * i], lo[2 * i + 1]);
+            hi[i] = pk_max_h(hi[2 * i], hi[2 * i + 1]);
+        }
+    // a = {min of the low halves, max of the low halves}, b the same of the high halves
+    const uint32_t a = __builtin_amdgcn_perm(hi[0], lo[0], 0x05040100u);
+    const uint32_t b = __builtin_amdgcn_perm(hi[0], lo[0], 0x07060302u);
+    uint32_t v;
+    asm("v_pk_min_f16 %0, %1, %2 neg_lo:[0,0] neg_hi:[1,1]" : "=v"(v) : "v"(a), "v"(b));
+    if (K >= 2) v = pk_min_h(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));
+    if (K >= 4) v = pk_min_h(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));
+    if (K >= 8) v = pk_min_h(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+    if (K >= 16) v = pk_min_h(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+    if (K >= 32) v = pk_min_h(v, (uint32_t)__shfl_xor((int)v, 16));
+    if (K >= 64) v = pk_min_h(v, (uint32_t)__shfl_xor((int)v, 32));
+    mn = h2f(v & 0xffffu);
+    mx = -h2f(v >> 16);
+}
+
+// Sum x*s over a lane's E weights in binary64. Every product is exact; the sum is exact
+// unless the group's weights span more than about 2^11 in magnitude, and within an ulp of
+// binary64 then. Four chains keep the adds independent.
+template <int W>
+__device__ __forceinline__ double lane_sum_xs(const uint32_t (&xb)[W], double sd)
+{
+    static_assert(W % 2 == 0, "pairs per lane: even");
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        acc[(2 * i) & 3] = fma((double)h2f(xb[i] & 0xffffu), sd, acc[(2 * i) & 3]);
+        acc[(2 * i + 1) & 3] = fma((double)h2f(xb[i] >> 16), sd, acc[(2 * i + 1) & 3]);
+    }
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
 // LDS atomic swap of 8 bytes (ds_wrxchg_rtn_b64): stores v, returns the old contents.
 __device__ __forceinline__ uint64_t xchg_l(uint64_t *p, uint64_t v)
 {
@@ -213,11 +278,11 @@ struct Cfg {
     static constexpr int RC = GB >= 32 ? 128 : 64;  // ring capacity
     static constexpr int LDS_WAVE = 163840 / (4 * WAVES) / 1280 * 1280;
     static constexpr int LDS_FREE = LDS_WAVE - 4 * RC - (NBITS == 3 ? 64 * EB : 0) - 128;
-    // How groups move between lanes and slots. Groups up to 64 swap in place with LDS atomic
-    // exchanges (half the swaps, measured 10-13 % faster at g16-g64); larger groups move with
-    // 16-byte stores and loads through free slots and a spare slot (the exchanges of 256-byte
-    // groups measured 1.5-3 % slower at g128).
-    static constexpr bool XCHG = G <= 64 && KP == 1;
+    // How groups move between lanes and slots. A group held by one lane (g16-g128 in the wide
+    // layout) swaps in place with LDS atomic exchanges: half the swaps, measured 10-13 % faster
+    // at g16-g64 and 12 % at g128. Groups spread over several lanes (g256, the narrow layout)
+    // move with 16-byte stores and loads through free slots and a spare slot.
+    static constexpr bool XCHG = KP == 1;
     static_assert(!XCHG || KP == 1, "in-place swaps move one lane per group");
     // one more column of weights (for an odd stride) comes out of the budget first, and with
     // the spare slot two whole slots
@@ -1048,27 +1113,12 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                 xb[4 * i + 2] = v.z;
                 xb[4 * i + 3] = v.w;
             }
-            // min / max on binary16 pairs, then across the group
-            h2v hmn = __builtin_bit_cast(h2v, xb[0]), hmx = hmn;
-#pragma unroll
-            for (int i = 1; i < WB; ++i) {
-                const h2v h = __builtin_bit_cast(h2v, xb[i]);
-                hmn = __builtin_elementwise_min(hmn, h);
-                hmx = __builtin_elementwise_max(hmx, h);
-            }
-            float mn = fminf((float)hmn.x, (float)hmn.y);
-            float mx = fmaxf((float)hmx.x, (float)hmx.y);
-            mn = minf_k<KB>(mn);
-            mx = maxf_k<KB>(mx);
+            float mn, mx;
+            group_min_max<WB, KB>(xb, mn, mx);
             const float rng = mx - mn;
             const float s = rng > 0.0f ? C::QMAX / rng : 1.0f;
             const float z0 = 0.0f - mn * s;      // +0 when min is a zero of either sign
-            const double sd = s;
-            double sxs = 0.0;
-#pragma unroll
-            for (int i = 0; i < EB; ++i)
-                sxs = fma((double)h2f(i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu), sd, sxs);
-            sxs = addd_k<KB>(sxs);
+            const double sxs = addd_k<KB>(lane_sum_xs<WB>(xb, (double)s));
             if (bleader) {
                 // The scale is fixed from here on: the tile's scales are stored now, one
                 // contiguous run per tile, rather than one by one as groups finish.
@@ -1164,25 +1214,12 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
     const double pm1 = (double)a.p - 1.0;
 
     // ---- INIT: min / max on binary16 pairs, s, z0, exact sum x*s ----
-    h2v hmn = __builtin_bit_cast(h2v, xb[0]), hmx = hmn;
-#pragma unroll
-    for (int i = 1; i < WB; ++i) {
-        const h2v h = __builtin_bit_cast(h2v, xb[i]);
-        hmn = __builtin_elementwise_min(hmn, h);
-        hmx = __builtin_elementwise_max(hmx, h);
-    }
-    float mn = fminf((float)hmn.x, (float)hmn.y);
-    float mx = fmaxf((float)hmx.x, (float)hmx.y);
-    mn = minf_k<KB>(mn);
-    mx = maxf_k<KB>(mx);
+    float mn, mx;
+    group_min_max<WB, KB>(xb, mn, mx);
     const float rng = mx - mn;
     const float s = rng > 0.0f ? C::QMAX / rng : 1.0f;
     const double sd = s;
-    double X = 0.0;
-#pragma unroll
-    for (int i = 0; i < EB; ++i)
-        X = fma((double)h2f(i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu), sd, X);
-    X = addd_k<KB>(X);
+    const double X = addd_k<KB>(lane_sum_xs<WB>(xb, sd));
     if (valid && bleader) gbl(J.scale)[gidx] = f2h(1.0f / s);
     // binary32 range test of the fast path: u of the extreme weights stays in range
     const float umn = mn, umx = mx;
