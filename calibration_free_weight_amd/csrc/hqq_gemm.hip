@@ -42,6 +42,14 @@ __device__ __forceinline__ uint16_t g_f2h(float f)
     asm("" : "+v"(f));
     return __half_as_ushort(__float2half_rn(f));
 }
+// Two such conversions packed into one word (a in the low half): one v_cvt_pk_f16_f32, which
+// the compiler does not always form from two single conversions joined by shifts.
+typedef float g2f __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t g_f2h2(float a, float b)
+{
+    asm("" : "+v"(a), "+v"(b));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(g2f{a, b}, h2));
+}
 
 struct QW {                      // a packed axis-1 quantized weight [N, K]
     const uint8_t *packed;
@@ -112,8 +120,7 @@ __device__ __forceinline__ void recon32(const QW &w, int64_t n, int64_t k0, floa
         const float zf = zero_of(w, gi, m0, m1), s = g_h2f(w.scale[gi]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            out[4 * c + i] = (uint32_t)g_f2h(((float)q[8 * c + 2 * i] - zf) * s) |
-                             (uint32_t)g_f2h(((float)q[8 * c + 2 * i + 1] - zf) * s) << 16;
+            out[4 * c + i] = g_f2h2(((float)q[8 * c + 2 * i] - zf) * s, ((float)q[8 * c + 2 * i + 1] - zf) * s);
     }
 }
 
@@ -204,8 +211,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(const uint16_t *__restrict__ 
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     wp[i] = __builtin_bit_cast(
-                        h2, (uint32_t)g_f2h(((float)q[it][8 * c + 2 * i] - zf[it][c]) * sc[it][c]) |
-                                (uint32_t)g_f2h(((float)q[it][8 * c + 2 * i + 1] - zf[it][c]) * sc[it][c]) << 16);
+                        h2, g_f2h2(((float)q[it][8 * c + 2 * i] - zf[it][c]) * sc[it][c], ((float)q[it][8 * c + 2 * i + 1] - zf[it][c]) * sc[it][c]));
 #pragma unroll
                 for (int m = 0; m < MB; ++m) {
                     if (m >= M) break;
@@ -370,8 +376,7 @@ __global__ void __launch_bounds__(256) gemv2_kernel(const uint16_t *__restrict__
                 for (int q = 0; q < 16; ++q) {      // pairs of codes
                     const int h = q >> 3;
                     const h2 wp = __builtin_bit_cast(
-                        h2, (uint32_t)g_f2h((c[2 * q] - zf[h]) * sc[h]) |
-                                (uint32_t)g_f2h((c[2 * q + 1] - zf[h]) * sc[h]) << 16);
+                        h2, g_f2h2((c[2 * q] - zf[h]) * sc[h], (c[2 * q + 1] - zf[h]) * sc[h]));
 #pragma unroll
                     for (int m = 0; m < MB; ++m) {
                         const uint32_t xw = xv[it][m][q >> 2][q & 3];
@@ -459,8 +464,7 @@ __device__ __forceinline__ void stage_store(const Stage<NB> &st, const QW &w, in
         for (int i = 0; i < 4; ++i) {
             const bool ok = st.wv && k0 + c + 8 * cc < w.K;
             out[4 * cc + i] =
-                ok ? (uint32_t)g_f2h(((float)q[8 * cc + 2 * i] - st.zf[cc]) * st.s[cc]) |
-                         (uint32_t)g_f2h(((float)q[8 * cc + 2 * i + 1] - st.zf[cc]) * st.s[cc]) << 16
+                ok ? g_f2h2(((float)q[8 * cc + 2 * i] - st.zf[cc]) * st.s[cc], ((float)q[8 * cc + 2 * i + 1] - st.zf[cc]) * st.s[cc])
                    : 0u;
         }
 #pragma unroll
@@ -610,8 +614,7 @@ __global__ void __launch_bounds__(256) recon_kernel(QW w, int64_t n, int64_t col
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int a = AX0 ? 2 * i : 0, b = AX0 ? 2 * i + 1 : 0;
-                o[i] = (uint32_t)g_f2h(((float)q[k][2 * i] - zf[k][a]) * sc[k][a]) |
-                       (uint32_t)g_f2h(((float)q[k][2 * i + 1] - zf[k][b]) * sc[k][b]) << 16;
+                o[i] = g_f2h2(((float)q[k][2 * i] - zf[k][a]) * sc[k][a], ((float)q[k][2 * i + 1] - zf[k][b]) * sc[k][b]);
             }
             const g4u v{o[0], o[1], o[2], o[3]};
             if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<g4u *>(Wr + u * 8));
@@ -935,7 +938,7 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
         uint32_t bw[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            bw[i] = (uint32_t)g_f2h((c[2 * i] - zf) * sc) | (uint32_t)g_f2h((c[2 * i + 1] - zf) * sc) << 16;
+            bw[i] = g_f2h2((c[2 * i] - zf) * sc, (c[2 * i + 1] - zf) * sc);
         const h8 b = __builtin_bit_cast(h8, g4u{bw[0], bw[1], bw[2], bw[3]});
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
