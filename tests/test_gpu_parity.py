@@ -282,3 +282,43 @@ def test_batch_equals_single_calls(O, dev):
         if zb == 8:
             assert torch.equal(o["zero_meta"], single["zero_meta"])
         compare(O, W, o, b, g, zb, label=f"batch b{b} g{g}")
+
+
+@pytest.mark.parametrize("layout", [1, 3, 0], ids=["persistent", "lockstep", "auto"])
+def test_repeated_solves_are_identical(dev, layout):
+    """The persistent solver claims tiles and moves groups between lanes in whatever order
+    its waves reach them; the outputs must not depend on that order. The same mixed batch is
+    solved five times over sentinel-filled outputs and every run must write the same bytes."""
+    specs = [(4096, 4096, 4, 128, 8), (2048, 4096, 2, 16, 8), (1024, 2048, 3, 64, 8),
+             (512, 4096, 4, 64, 16), (256, 1024, 8, 32, 16)]
+    Ws, outs, jobs = [], [], []
+    for i, (r, c, b, g, zb) in enumerate(specs):
+        W = weights(r, c, 1700 + i, dev)
+        o = hqq.alloc_outputs(r, c, b, g, zb, dev, passes=True)
+        jobs.append(hqq.make_job(W, b, g, 1, 0.7, 1.0, 1.01, 20, 1, zb, o["packed"], o["scale"],
+                                 o["zero"], o["zero_meta"], o["passes"]))
+        Ws.append(W)
+        outs.append(o)
+    ws = hqq.alloc_workspace(jobs, dev)
+    keys = ("packed", "scale", "zero", "passes")
+    try:
+        hqq.hqq_debug_solver(pass_layout=layout)
+        first = None
+        for run_i in range(5):
+            print(f"repeat layout={layout} run {run_i}", flush=True)
+            for o in outs:
+                for k, v in zip(keys, (0x5A, 0, 0x33, 0xEE)):
+                    o[k].view(torch.uint8).fill_(v)
+            torch.cuda.synchronize()
+            hqq.hqq_quantize_batch(jobs, ws)
+            torch.cuda.synchronize()
+            hqq.hqq_batch_check(jobs, ws)
+            cur = [{k: o[k].clone() for k in keys + ("zero_meta",) if o[k] is not None} for o in outs]
+            if first is None:
+                first = cur
+                continue
+            for i, (a, b) in enumerate(zip(first, cur)):
+                for k in a:
+                    assert torch.equal(a[k], b[k]), f"run {run_i} tensor {i} {k} differs"
+    finally:
+        hqq.hqq_debug_solver()
