@@ -292,6 +292,55 @@ def dequant_row(specs, outs, dev, stream, reps=5):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def fused_gemm_row(specs, outs, Xs, Ys, eager, stream, reps, nbytes, flops):
+    """The same layers, with the projections that read one input multiplied by one
+    hqq_gemm_multi call each (per block: q, k and v; gate and up; o and down alone), as an
+    inference engine runs them: fewer, fuller launches. Graph-captured like the per-layer
+    row and checked equal to its outputs."""
+    import torch
+    from calibration_free_weight_amd import hqq
+    by_block = {}
+    for s, o, Y in zip(specs, outs, Ys):
+        by_block.setdefault(s.block, []).append((s, o, Y))
+    calls = []
+    for b in sorted(by_block):
+        layers = sorted(by_block[b], key=lambda t: t[0].proj)
+        for group in ((0, 1, 2), (3,), (4, 5), (6,)):
+            members = [(s, o, Y) for s, o, Y in layers if s.proj in group]
+            if members:
+                weights = [dict(packed=o["packed"], scale=o["scale"], zero=o["zero"],
+                                zero_meta=o["zero_meta"], N=s.rows, nbits=s.nbits,
+                                group_size=s.group_size, zero_bits=s.zero_bits, Y=Y)
+                           for s, o, Y in members]
+                calls.append((Xs[members[0][0].cols], weights))
+
+    def run_all():
+        for X, weights in calls:
+            hqq.hqq_gemm_multi(X, weights)
+    for Y in Ys:
+        Y.fill_(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    for _ in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(eager, Ys)), "fused layers differ"
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms_per_stack": round(ms, 4), "graph": True, "calls": len(calls),
+            "hbm_gbs": round(gbs, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def gemm_row(specs, outs, dev, stream, reps=5, graphs=True):
     """The quantized linear layers of the stack (hqq_gemm on the 224 quantized weights the
     benchmark just wrote). Decode, M = 1, and small batches, M = 16 and 64 (the weight
@@ -358,6 +407,9 @@ def gemm_row(specs, outs, dev, stream, reps=5, graphs=True):
             row.update(bound="mfma", achieved=row["tflops"], peak=2500.0, unit="TFLOP/s",
                        frac=round(row["tflops"] / 2500.0, 4))
         res[f"m{m}"] = row
+        if m <= 64 and graphs:
+            res[f"m{m}_fused"] = fused_gemm_row(specs, outs, Xs, Ys, eager, stream, reps, nbytes,
+                                                flops)
         del X, Ys, eager, Xs, ws
 
     # Prefill with W_r resident: every layer's weight reconstructed once by hqq_dequantize

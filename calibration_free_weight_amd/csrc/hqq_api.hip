@@ -668,6 +668,29 @@ size_t hqq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
     return hqq::gemm_workspace_bytes(M, N, K);
 }
 
+namespace {
+// Argument checks of one weight of hqq_gemm / hqq_gemm_multi (M > 0, N > 0).
+hqq_status check_gemm_weight(const void *packed, const void *scale, const void *zero,
+                             const void *zero_meta, int64_t N, int64_t K, int nbits,
+                             int group_size, int zero_bits, const void *Y, const char *what)
+{
+    hqq_status st = check_layout(N, K, nbits, group_size, 1, what);
+    if (st != HQQ_OK) return st;
+    if (zero_bits != 8 && zero_bits != 16)
+        return fail(HQQ_ERR_ARG, std::string(what) + "zero_bits must be 8 or 16");
+    if (!Y || (K > 0 && (!packed || !scale || !zero)))
+        return fail(HQQ_ERR_ARG, std::string(what) + "Y, packed, scale and zero must be non-null");
+    if (zero_bits == 8 && K > 0 && !zero_meta)
+        return fail(HQQ_ERR_ARG, std::string(what) + "zero_meta must be non-null when zero_bits == 8");
+    if (!aligned(Y, 2) || !aligned(scale, 2) || (zero_bits == 16 && !aligned(zero, 2)) ||
+        (zero_bits == 8 && !aligned(zero_meta, 2)))
+        return fail(HQQ_ERR_ARG, std::string(what) + "binary16 buffers must be 2-byte aligned");
+    if (nbits == 3 && !aligned(packed, 4))
+        return fail(HQQ_ERR_ARG, std::string(what) + "packed must be 4-byte aligned");
+    return HQQ_OK;
+}
+}  // namespace
+
 hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *scale,
                     const void *zero, const void *zero_meta, int64_t N, int64_t K, int nbits,
                     int group_size, int zero_bits, void *Y, void *workspace,
@@ -679,15 +702,10 @@ hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *sc
     if (M > 0 && K > (int64_t(1) << 40) / M) return fail(HQQ_ERR_ARG, "M*K too large");
     if (zero_bits != 8 && zero_bits != 16) return fail(HQQ_ERR_ARG, "zero_bits must be 8 or 16");
     if (M == 0 || N == 0) return HQQ_OK;
-    if (!X || !Y || (K > 0 && (!packed || !scale || !zero)))
-        return fail(HQQ_ERR_ARG, "X, Y, packed, scale and zero must be non-null");
-    if (zero_bits == 8 && K > 0 && !zero_meta)
-        return fail(HQQ_ERR_ARG, "zero_meta must be non-null when zero_bits == 8");
+    if (!X) return fail(HQQ_ERR_ARG, "X, Y, packed, scale and zero must be non-null");
+    st = check_gemm_weight(packed, scale, zero, zero_meta, N, K, nbits, group_size, zero_bits, Y, "");
+    if (st != HQQ_OK) return st;
     if (!aligned(X, 16)) return fail(HQQ_ERR_ARG, "X must be 16-byte aligned");
-    if (!aligned(Y, 2) || !aligned(scale, 2) || (zero_bits == 16 && !aligned(zero, 2)) ||
-        (zero_bits == 8 && !aligned(zero_meta, 2)))
-        return fail(HQQ_ERR_ARG, "binary16 buffers must be 2-byte aligned");
-    if (nbits == 3 && !aligned(packed, 4)) return fail(HQQ_ERR_ARG, "packed must be 4-byte aligned");
     const size_t need = hqq::gemm_workspace_bytes(M, N, K);
     if (workspace && need > 0 && workspace_bytes < need)
         return fail(HQQ_ERR_WORKSPACE, "workspace smaller than hqq_gemm_workspace_bytes(M, N, K)");
@@ -700,6 +718,52 @@ hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *sc
                                     group_size, zero_bits, static_cast<uint16_t *>(Y),
                                     need > 0 ? static_cast<uint16_t *>(workspace) : nullptr,
                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_fail(e, "gemm launch");
+    g_last_error.clear();
+    return HQQ_OK;
+}
+
+hqq_status hqq_gemm_multi(const void *X, int64_t M, int64_t K, const hqq_gemm_weight *weights,
+                          int n_weights, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (M < 0 || K < 0 || n_weights < 0) return fail(HQQ_ERR_ARG, "M, K and n_weights must be >= 0");
+    if (M > 0 && K > (int64_t(1) << 40) / M) return fail(HQQ_ERR_ARG, "M*K too large");
+    if (n_weights > 0 && !weights) return fail(HQQ_ERR_ARG, "weights must be non-null");
+    size_t need = 0;
+    std::vector<hqq::GemmWeight> ws;
+    for (int i = 0; i < n_weights; ++i) {
+        const hqq_gemm_weight &w = weights[i];
+        const std::string what = "weight " + std::to_string(i) + ": ";
+        hqq_status st = check_layout(w.N, K, w.nbits, w.group_size, 1, what.c_str());
+        if (st != HQQ_OK) return st;
+        if (w.zero_bits != 8 && w.zero_bits != 16)
+            return fail(HQQ_ERR_ARG, what + "zero_bits must be 8 or 16");
+        if (M == 0 || w.N == 0) continue;
+        st = check_gemm_weight(w.packed, w.scale, w.zero, w.zero_meta, w.N, K, w.nbits,
+                               w.group_size, w.zero_bits, w.Y, what.c_str());
+        if (st != HQQ_OK) return st;
+        const size_t nd = hqq::gemm_workspace_bytes(M, w.N, K);
+        need = nd > need ? nd : need;
+        ws.push_back(hqq::GemmWeight{static_cast<const uint8_t *>(w.packed),
+                                     static_cast<const uint16_t *>(w.scale), w.zero,
+                                     static_cast<const uint16_t *>(w.zero_meta), w.N, w.nbits,
+                                     w.group_size, w.zero_bits, static_cast<uint16_t *>(w.Y)});
+    }
+    if (ws.empty()) {
+        g_last_error.clear();
+        return HQQ_OK;
+    }
+    if (!X) return fail(HQQ_ERR_ARG, "X must be non-null");
+    if (!aligned(X, 16)) return fail(HQQ_ERR_ARG, "X must be 16-byte aligned");
+    if (workspace && need > 0 && workspace_bytes < need)
+        return fail(HQQ_ERR_WORKSPACE,
+                    "workspace smaller than the largest hqq_gemm_workspace_bytes(M, N_i, K)");
+    if (workspace && !aligned(workspace, 16))
+        return fail(HQQ_ERR_ARG, "workspace must be 16-byte aligned");
+    hipError_t e = hqq::launch_gemm_multi(static_cast<const uint16_t *>(X), M, K, ws.data(),
+                                          (int)ws.size(),
+                                          need > 0 ? static_cast<uint16_t *>(workspace) : nullptr,
+                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_fail(e, "gemm launch");
     g_last_error.clear();
     return HQQ_OK;

@@ -21,6 +21,8 @@
 #include <hip/hip_fp16.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "hqq_internal.h"
 
 namespace hqq {
@@ -59,6 +61,24 @@ struct QW {                      // a packed axis-1 quantized weight [N, K]
     int64_t N, K;
     int g_log2, zero_bits;
 };
+
+// Weights that read the same X, multiplied by one launch of the decode or skinny kernel: the
+// grid is the weights' grids one after another, and a block finds its weight by its index.
+constexpr int kMaxSet = 8;
+struct QWSet {
+    QW w[kMaxSet];
+    uint16_t *Y[kMaxSet];
+    uint32_t b0[kMaxSet + 1];    // first block of each weight; b0[n] = all blocks
+    int n;
+};
+// The block's weight, and blk turned into the block's index among that weight's blocks.
+__device__ __forceinline__ int set_pick(const QWSet &s, uint32_t &blk)
+{
+    int i = 0;
+    while (i + 1 < s.n && blk >= s.b0[i + 1]) ++i;
+    blk -= s.b0[i];
+    return i;
+}
 
 // Codes k0 .. k0+31 of row n (k0 a multiple of 16; codes past K read as 0 and are never
 // used). NB in {1, 2, 4, 8}: a row starts on a byte (K is a multiple of 16), so the 32 codes
@@ -299,14 +319,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 }
 
 template <int NB, int MB, int R, int ZB, int ITV = 0>
-__global__ void __launch_bounds__(256) gemv2_kernel(const uint16_t *__restrict__ X, int M, QW w,
-                                                    uint16_t *__restrict__ Y)
+__global__ void __launch_bounds__(256) gemv2_kernel(const uint16_t *__restrict__ X, int M,
+                                                    QWSet set)
 {
+    uint32_t blk = blockIdx.x;
+    const int wi = set_pick(set, blk);
+    const QW w = set.w[wi];
+    uint16_t *__restrict__ const Y = set.Y[wi];
     constexpr int zb = ZB / 8;                   // bytes per stored zero
     constexpr uint32_t kOut = 0x80000000u;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
-    const int64_t n0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+    const int64_t n0 = ((int64_t)blk * 4 + wave) * R;
     if (n0 >= w.N) return;                       // whole wave
     const int64_t rows = w.N - n0 < R ? w.N - n0 : R;
     const int64_t rb = w.K * NB / 8;             // packed bytes per row (a multiple of 4)
@@ -875,15 +899,18 @@ struct SkinnySlot {
 
 template <int NB, int MT, int ZB>
 __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__restrict__ X,
-                                                          int64_t M, QW w,
-                                                          uint16_t *__restrict__ Y)
+                                                          int64_t M, QWSet set)
 {
+    uint32_t blk = blockIdx.x;
+    const int wi = set_pick(set, blk);
+    const QW w = set.w[wi];
+    uint16_t *__restrict__ const Y = set.Y[wi];
     constexpr uint32_t kOut = 0x80000000u;
     constexpr int ST = 8, D = 4;                 // waves per block; steps of loads in flight
     __shared__ float red[(ST - 1) * MT * 4 * 64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n0 = (int64_t)blk * 16;
     // MFMA fragment layout: lane t holds row t % 16, k-piece t / 16 (8 k) of a step. Loads
     // use lane l = 4 * row + piece instead, so 4 neighbouring lanes read one contiguous run
     // (the fragment layout puts neighbours in different rows, and the texture addresser
@@ -975,42 +1002,73 @@ __global__ void __launch_bounds__(512) gemm_skinny_kernel(const uint16_t *__rest
         }
 }
 
-template <int NB, int ZB>
-void launch_skinny_zb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStream_t stream)
+// Launches a kernel over the weights w[0..n) (outputs Y[0..n)), up to kMaxSet per launch:
+// blocks(w) is a weight's grid, go(grid, set) the launch.
+template <typename B, typename L>
+void launch_sets(const QW *w, uint16_t *const *Y, int n, B blocks, L go)
 {
-    const dim3 grid((unsigned)((w.N + 15) / 16)), block(512);
-    if (M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<NB, 1, ZB>), grid, block, 0, stream, X, M, w, Y);
-    else if (M <= 32) hipLaunchKernelGGL((gemm_skinny_kernel<NB, 2, ZB>), grid, block, 0, stream, X, M, w, Y);
-    else if (M <= 48) hipLaunchKernelGGL((gemm_skinny_kernel<NB, 3, ZB>), grid, block, 0, stream, X, M, w, Y);
-    else hipLaunchKernelGGL((gemm_skinny_kernel<NB, 4, ZB>), grid, block, 0, stream, X, M, w, Y);
+    for (int o = 0; o < n; o += kMaxSet) {
+        QWSet set{};
+        uint32_t total = 0;
+        for (int i = o; i < n && i < o + kMaxSet; ++i) {
+            set.w[set.n] = w[i];
+            set.Y[set.n] = Y[i];
+            set.b0[set.n] = total;
+            total += (uint32_t)blocks(w[i]);
+            ++set.n;
+        }
+        set.b0[set.n] = total;
+        if (total > 0) go(dim3(total), set);
+    }
+}
+
+template <int NB, int ZB>
+void launch_skinny_zb(const uint16_t *X, int64_t M, const QW *w, uint16_t *const *Y, int n,
+                      hipStream_t stream)
+{
+    const dim3 block(512);
+    auto blocks = [](const QW &q) { return (q.N + 15) / 16; };
+    launch_sets(w, Y, n, blocks, [&](dim3 grid, const QWSet &set) {
+        if (M <= 16) hipLaunchKernelGGL((gemm_skinny_kernel<NB, 1, ZB>), grid, block, 0, stream, X, M, set);
+        else if (M <= 32) hipLaunchKernelGGL((gemm_skinny_kernel<NB, 2, ZB>), grid, block, 0, stream, X, M, set);
+        else if (M <= 48) hipLaunchKernelGGL((gemm_skinny_kernel<NB, 3, ZB>), grid, block, 0, stream, X, M, set);
+        else hipLaunchKernelGGL((gemm_skinny_kernel<NB, 4, ZB>), grid, block, 0, stream, X, M, set);
+    });
 }
 
 template <int NB>
-void launch_skinny(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStream_t stream)
+void launch_skinny(const uint16_t *X, int64_t M, const QW *w, uint16_t *const *Y, int n,
+                   hipStream_t stream)
 {
-    if (w.zero_bits == 8) launch_skinny_zb<NB, 8>(X, M, w, Y, stream);
-    else launch_skinny_zb<NB, 16>(X, M, w, Y, stream);
+    if (w[0].zero_bits == 8) launch_skinny_zb<NB, 8>(X, M, w, Y, n, stream);
+    else launch_skinny_zb<NB, 16>(X, M, w, Y, n, stream);
 }
 
 template <int NB, int ZB>
-void launch_gemv2(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, hipStream_t stream)
+void launch_gemv2(const uint16_t *X, int64_t M, const QW *w, uint16_t *const *Y, int n,
+                  hipStream_t stream)
 {
     const dim3 block(256);
+    const int64_t K = w[0].K;
     if (M == 1) {
         constexpr int R = kGemvRows;
-        const dim3 grid((unsigned)((w.N + 4 * R - 1) / (4 * R)));
+        auto blocks = [](const QW &q) { return (q.N + 4 * R - 1) / (4 * R); };
         // rows of more than two chunks per lane keep three in flight (the 11008-wide rows of
         // an MLP down projection then take two load rounds instead of three; six were slower)
-        if (((w.K + 2047) >> 11) > 2)
-            hipLaunchKernelGGL((gemv2_kernel<NB, 1, R, ZB, 3>), grid, block, 0, stream, X, (int)M, w, Y);
-        else
-            hipLaunchKernelGGL((gemv2_kernel<NB, 1, R, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
+        launch_sets(w, Y, n, blocks, [&](dim3 grid, const QWSet &set) {
+            if (((K + 2047) >> 11) > 2)
+                hipLaunchKernelGGL((gemv2_kernel<NB, 1, R, ZB, 3>), grid, block, 0, stream, X, (int)M, set);
+            else
+                hipLaunchKernelGGL((gemv2_kernel<NB, 1, R, ZB>), grid, block, 0, stream, X, (int)M, set);
+        });
         return;
     }
-    const dim3 grid((unsigned)((w.N + 3) / 4));
-    if (M == 2) hipLaunchKernelGGL((gemv2_kernel<NB, 2, 1, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
-    else if (M <= 4) hipLaunchKernelGGL((gemv2_kernel<NB, 4, 1, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
-    else hipLaunchKernelGGL((gemv2_kernel<NB, 8, 1, ZB>), grid, block, 0, stream, X, (int)M, w, Y);
+    auto blocks = [](const QW &q) { return (q.N + 3) / 4; };
+    launch_sets(w, Y, n, blocks, [&](dim3 grid, const QWSet &set) {
+        if (M == 2) hipLaunchKernelGGL((gemv2_kernel<NB, 2, 1, ZB>), grid, block, 0, stream, X, (int)M, set);
+        else if (M <= 4) hipLaunchKernelGGL((gemv2_kernel<NB, 4, 1, ZB>), grid, block, 0, stream, X, (int)M, set);
+        else hipLaunchKernelGGL((gemv2_kernel<NB, 8, 1, ZB>), grid, block, 0, stream, X, (int)M, set);
+    });
 }
 
 // Y = X . Wr^T for a binary16 Wr [N, K] (K a multiple of 8, at most kMaxWsK).
@@ -1031,33 +1089,81 @@ void launch_f16(const uint16_t *X, int64_t M, const uint16_t *Wr, int64_t N, int
                            stream, X, M, Wr, N, K, Y);
 }
 
+// The kernel a weight takes for M rows of X (and a workspace Wr, or none).
+enum GemmPath { kPathRecon, kPathSkinny, kPathGemv2, kPathGemv, kPathTiles };
 template <int NB>
-void launch_nb(const uint16_t *X, int64_t M, const QW &w, uint16_t *Y, uint16_t *Wr,
+GemmPath path_of(const QW &w, int64_t M, const uint16_t *Wr)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(w.packed);
+    if (M > kWsM && Wr && recon_fits(w.packed, NB, w.K, 1, Wr)) return kPathRecon;
+    if (M > kSkinnyLo && 64 * w.K * 2 < 0x7FFFFFF0 &&
+        (pa & (NB == 8 ? 7 : NB == 1 ? 0 : NB == 2 ? 1 : 3)) == 0)
+        return kPathSkinny;
+    if (M <= kSkinnyM && NB != 3 && (w.K * NB) % 32 == 0 && (pa & 3) == 0 &&
+        M * w.K * 2 < 0x7FFFFFF0 && 4 * (w.K * NB / 8) < 0x7FFFFFF0)
+        return kPathGemv2;
+    return M <= kSkinnyM ? kPathGemv : kPathTiles;
+}
+
+// Weights w[0..n) of one bit width and one K, all multiplied by the same X. Those that take
+// the skinny or decode kernel share launches (by zero storage); the others go one by one,
+// reusing the workspace Wr in turn.
+template <int NB>
+void launch_nb(const uint16_t *X, int64_t M, const QW *w, uint16_t *const *Y, int n, uint16_t *Wr,
                hipStream_t stream)
 {
+    const int64_t K = w[0].K;
+    for (const int zb : {8, 16}) {
+        for (const GemmPath pth : {kPathSkinny, kPathGemv2}) {
+            std::vector<QW> sw;
+            std::vector<uint16_t *> sy;
+            for (int i = 0; i < n; ++i)
+                if (w[i].zero_bits == zb && path_of<NB>(w[i], M, Wr) == pth) {
+                    sw.push_back(w[i]);
+                    sy.push_back(Y[i]);
+                }
+            if (sw.empty()) continue;
+            const int m = (int)sw.size();
+            if (pth == kPathSkinny) {
+                // up to 64 rows per launch; more rows (no workspace) in slices of 64
+                std::vector<uint16_t *> ys(m);
+                for (int64_t m0 = 0; m0 < M; m0 += 64) {
+                    for (int j = 0; j < m; ++j) ys[j] = sy[j] + m0 * sw[j].N;
+                    launch_skinny<NB>(X + m0 * K, M - m0 < 64 ? M - m0 : 64, sw.data(), ys.data(), m,
+                                      stream);
+                }
+            } else if (zb == 8) {
+                launch_gemv2<NB, 8>(X, M, sw.data(), sy.data(), m, stream);
+            } else {
+                launch_gemv2<NB, 16>(X, M, sw.data(), sy.data(), m, stream);
+            }
+        }
+    }
     const dim3 block(256);
-    if (M > kWsM && Wr && recon_fits(w.packed, NB, w.K, 1, Wr)) {   // packed aligned for its loads
-        launch_recon_nb<NB>(w, w.N * w.K, w.K, 1, false, Wr, stream);   // N*K: a multiple of 16
-        launch_f16(X, M, Wr, w.N, w.K, Y, stream);
-    } else if (M > kSkinnyLo && 64 * w.K * 2 < 0x7FFFFFF0 &&
-               (reinterpret_cast<uintptr_t>(w.packed) & (NB == 8 ? 7 : NB == 1 ? 0 : NB == 2 ? 1 : 3)) == 0) {
-        // up to 64 rows per launch; more rows (no workspace) in slices of 64
-        for (int64_t m0 = 0; m0 < M; m0 += 64)
-            launch_skinny<NB>(X + m0 * w.K, M - m0 < 64 ? M - m0 : 64, w, Y + m0 * w.N, stream);
-    } else if (M <= kSkinnyM && NB != 3 && (w.K * NB) % 32 == 0 &&
-               (reinterpret_cast<uintptr_t>(w.packed) & 3) == 0 && M * w.K * 2 < 0x7FFFFFF0 &&
-               4 * (w.K * NB / 8) < 0x7FFFFFF0) {
-        if (w.zero_bits == 8) launch_gemv2<NB, 8>(X, M, w, Y, stream);
-        else launch_gemv2<NB, 16>(X, M, w, Y, stream);
-    } else if (M <= kSkinnyM) {
-        const dim3 grid((unsigned)((w.N + 3) / 4));
-        if (M == 1) hipLaunchKernelGGL((gemv_kernel<NB, 1>), grid, block, 0, stream, X, (int)M, w, Y);
-        else if (M == 2) hipLaunchKernelGGL((gemv_kernel<NB, 2>), grid, block, 0, stream, X, (int)M, w, Y);
-        else if (M <= 4) hipLaunchKernelGGL((gemv_kernel<NB, 4>), grid, block, 0, stream, X, (int)M, w, Y);
-        else hipLaunchKernelGGL((gemv_kernel<NB, 8>), grid, block, 0, stream, X, (int)M, w, Y);
-    } else {
-        const int64_t blocks = ((M + BM - 1) / BM) * ((w.N + BN - 1) / BN);
-        hipLaunchKernelGGL((gemm_mfma_kernel<NB>), dim3((unsigned)blocks), block, 0, stream, X, M, w, Y);
+    for (int i = 0; i < n; ++i) {
+        const QW &q = w[i];
+        uint16_t *const y = Y[i];
+        switch (path_of<NB>(q, M, Wr)) {
+        case kPathRecon:
+            launch_recon_nb<NB>(q, q.N * K, K, 1, false, Wr, stream);   // N*K: a multiple of 16
+            launch_f16(X, M, Wr, q.N, K, y, stream);
+            break;
+        case kPathGemv: {
+            const dim3 grid((unsigned)((q.N + 3) / 4));
+            if (M == 1) hipLaunchKernelGGL((gemv_kernel<NB, 1>), grid, block, 0, stream, X, (int)M, q, y);
+            else if (M == 2) hipLaunchKernelGGL((gemv_kernel<NB, 2>), grid, block, 0, stream, X, (int)M, q, y);
+            else if (M <= 4) hipLaunchKernelGGL((gemv_kernel<NB, 4>), grid, block, 0, stream, X, (int)M, q, y);
+            else hipLaunchKernelGGL((gemv_kernel<NB, 8>), grid, block, 0, stream, X, (int)M, q, y);
+            break;
+        }
+        case kPathTiles: {
+            const int64_t blocks = ((M + BM - 1) / BM) * ((q.N + BN - 1) / BN);
+            hipLaunchKernelGGL((gemm_mfma_kernel<NB>), dim3((unsigned)blocks), block, 0, stream, X, M, q, y);
+            break;
+        }
+        default:
+            break;                               // launched above
+        }
     }
 }
 
@@ -1116,14 +1222,45 @@ hipError_t launch_gemm(const uint16_t *X, int64_t M, const uint8_t *packed, cons
     while ((1 << lg) < g) ++lg;
     const QW w{packed, scale, zero, zero_bits == 8 ? zero_meta : nullptr, N, K, lg, zero_bits};
     switch (nbits) {
-    case 1: launch_nb<1>(X, M, w, Y, Wr, stream); break;
-    case 2: launch_nb<2>(X, M, w, Y, Wr, stream); break;
-    case 3: launch_nb<3>(X, M, w, Y, Wr, stream); break;
-    case 4: launch_nb<4>(X, M, w, Y, Wr, stream); break;
-    case 8: launch_nb<8>(X, M, w, Y, Wr, stream); break;
+    case 1: launch_nb<1>(X, M, &w, &Y, 1, Wr, stream); break;
+    case 2: launch_nb<2>(X, M, &w, &Y, 1, Wr, stream); break;
+    case 3: launch_nb<3>(X, M, &w, &Y, 1, Wr, stream); break;
+    case 4: launch_nb<4>(X, M, &w, &Y, 1, Wr, stream); break;
+    case 8: launch_nb<8>(X, M, &w, &Y, 1, Wr, stream); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_multi(const uint16_t *X, int64_t M, int64_t K, const GemmWeight *ws, int n,
+                             uint16_t *Wr, hipStream_t stream)
+{
+    if (M == 0) return hipSuccess;
+    for (const int nbits : {1, 2, 3, 4, 8}) {
+        std::vector<QW> w;
+        std::vector<uint16_t *> Y;
+        for (int i = 0; i < n; ++i) {
+            const GemmWeight &g = ws[i];
+            if (g.nbits != nbits || g.N == 0) continue;
+            int lg = 0;
+            while ((1 << lg) < g.group_size) ++lg;
+            w.push_back(QW{g.packed, g.scale, g.zero, g.zero_bits == 8 ? g.zero_meta : nullptr, g.N,
+                           K, lg, g.zero_bits});
+            Y.push_back(g.Y);
+        }
+        if (w.empty()) continue;
+        const int m = (int)w.size();
+        switch (nbits) {
+        case 1: launch_nb<1>(X, M, w.data(), Y.data(), m, Wr, stream); break;
+        case 2: launch_nb<2>(X, M, w.data(), Y.data(), m, Wr, stream); break;
+        case 3: launch_nb<3>(X, M, w.data(), Y.data(), m, Wr, stream); break;
+        case 4: launch_nb<4>(X, M, w.data(), Y.data(), m, Wr, stream); break;
+        default: launch_nb<8>(X, M, w.data(), Y.data(), m, Wr, stream); break;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace hqq

@@ -111,6 +111,20 @@ hipError_t launch_gemm(const uint16_t *X, int64_t M, const uint8_t *packed, cons
                        const void *zero, const uint16_t *zero_meta, int64_t N, int64_t K,
                        int nbits, int g, int zero_bits, uint16_t *Y, uint16_t *Wr,
                        hipStream_t stream);
+// Several weights [N_i, K] multiplied by the same X (each exactly as launch_gemm would): the
+// weights that take the decode or skinny kernels share launches. Wr as in launch_gemm, large
+// enough for every weight that uses it (used in turn).
+struct GemmWeight {
+    const uint8_t *packed;
+    const uint16_t *scale;
+    const void *zero;
+    const uint16_t *zero_meta;
+    int64_t N;
+    int nbits, group_size, zero_bits;
+    uint16_t *Y;
+};
+hipError_t launch_gemm_multi(const uint16_t *X, int64_t M, int64_t K, const GemmWeight *w, int n,
+                             uint16_t *Wr, hipStream_t stream);
 
 // 8-bit scales: scale_group a power of two in [8, 512]; buffers 16-byte aligned (meta 4).
 hipError_t launch_scale_requant(const uint16_t *scale, int64_t n, int scale_group, uint8_t *sq,

@@ -21,7 +21,8 @@ EXPORTS = ("hqq_packed_bytes", "hqq_workspace_bytes", "hqq_quantize", "hqq_quant
            "hqq_streamed_workspace_bytes", "hqq_dequantize", "hqq_gemm",
            "hqq_gemm_workspace_bytes", "hqq_gemm_f16", "hqq_requant_scales",
            "hqq_dequantize_scales", "hqq_pack", "hqq_unpack", "hqq_status_string",
-           "hqq_last_error", "hqq_batch_check", "hqq_debug_solver", "hqq_quantize_noalloc")
+           "hqq_last_error", "hqq_batch_check", "hqq_debug_solver", "hqq_quantize_noalloc",
+           "hqq_gemm_multi")
 
 
 class HQQError(RuntimeError):
@@ -37,6 +38,12 @@ class hqq_job(C.Structure):
                 ("iters", C.c_int), ("early_stop", C.c_int), ("zero_bits", C.c_int),
                 ("packed", C.c_void_p), ("scale", C.c_void_p), ("zero", C.c_void_p),
                 ("zero_meta", C.c_void_p), ("passes", C.c_void_p)]
+
+
+class hqq_gemm_weight(C.Structure):
+    _fields_ = [("packed", C.c_void_p), ("scale", C.c_void_p), ("zero", C.c_void_p),
+                ("zero_meta", C.c_void_p), ("N", C.c_int64), ("nbits", C.c_int),
+                ("group_size", C.c_int), ("zero_bits", C.c_int), ("Y", C.c_void_p)]
 
 
 _L = None
@@ -79,6 +86,8 @@ def lib():
                                C.c_size_t, vp]
         L.hqq_gemm_workspace_bytes.restype = C.c_size_t
         L.hqq_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.hqq_gemm_multi.restype = i32
+        L.hqq_gemm_multi.argtypes = [vp, i64, i64, C.POINTER(hqq_gemm_weight), i32, vp, C.c_size_t, vp]
         L.hqq_gemm_f16.restype = i32
         L.hqq_gemm_f16.argtypes = [vp, i64, vp, i64, i64, vp, vp]
         L.hqq_requant_scales.restype = i32
@@ -229,6 +238,21 @@ def hqq_gemm(X, packed, scale, zero, zero_meta, N, K, nbits, group_size, zero_bi
     _check(lib().hqq_gemm(_p(X), M, _p(packed), _p(scale), _p(zero), _p(zero_meta), N, K,
                           nbits, group_size, zero_bits, _p(Y), _p(workspace), wb,
                           _stream(stream)))
+
+
+def hqq_gemm_multi(X, weights, workspace=None, stream=None) -> None:
+    """Several weights [N_i, K] multiplied by the same X: `weights` is a list of dicts with
+    packed, scale, zero, zero_meta, N, nbits, group_size, zero_bits and Y (as hqq_gemm's
+    arguments); each Y_i gets what hqq_gemm would write."""
+    M, K = X.shape
+    arr = (hqq_gemm_weight * max(len(weights), 1))()
+    for i, w in enumerate(weights):
+        arr[i] = hqq_gemm_weight(_p(w["packed"]), _p(w["scale"]), _p(w["zero"]),
+                                 _p(w.get("zero_meta")), w["N"], w["nbits"], w["group_size"],
+                                 w["zero_bits"], _p(w["Y"]))
+    wb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hqq_gemm_multi(_p(X), M, K, arr, len(weights), _p(workspace), wb,
+                                _stream(stream)))
 
 
 def hqq_gemm_workspace_bytes(M, N, K) -> int:

@@ -237,6 +237,34 @@ hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *sc
  * else 0 (no workspace is used). */
 size_t hqq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/* One weight of hqq_gemm_multi: hqq_gemm's per-weight arguments, and its output. */
+typedef struct hqq_gemm_weight {
+    const void *packed;      /* packed codes of the axis-1 quantized weight [N, K] */
+    const void *scale;       /* binary16 [N*K/group_size] */
+    const void *zero;        /* binary16, or uint8 with zero_bits == 8 */
+    const void *zero_meta;   /* binary16 {step, base} with zero_bits == 8, else ignored */
+    int64_t N;               /* rows of the weight = columns of its Y */
+    int nbits;               /* 1, 2, 3, 4 or 8 */
+    int group_size;          /* 16, 32, 64, 128 or 256 */
+    int zero_bits;           /* 16 or 8 */
+    void *Y;                 /* binary16 row-major [M, N] */
+} hqq_gemm_weight;
+
+/* Several linear layers that read one input [SK "HQQLinear layer", as hqq_gemm]: for each
+ * weight i, Y_i = X . W_r,i^T, bit for bit what hqq_gemm(X, M, weight i, K, Y_i) writes (the
+ * same kernel computes each weight's outputs the same way). Weights that share a bit width
+ * and zero storage and take the streaming kernels (M <= 64, word-aligned packed buffers)
+ * are multiplied by shared launches, up to eight weights each, so that layers such as an
+ * attention block's q, k and v projections, or an MLP's gate and up projections, fill the
+ * GPU together rather than one after another; the others are launched one by one. Every
+ * weight is [N_i, K] with the same K; X as in hqq_gemm; the Y_i must not overlap each other
+ * or X. n_weights = 0, M = 0 or N_i = 0 do nothing for those weights. workspace: as in
+ * hqq_gemm, at least the largest hqq_gemm_workspace_bytes(M, N_i, K), used by one weight
+ * after another; too small is HQQ_ERR_WORKSPACE. Argument errors name the weight; nothing is
+ * launched when any weight is invalid. Nothing is allocated on the device. */
+hqq_status hqq_gemm_multi(const void *X, int64_t M, int64_t K, const hqq_gemm_weight *weights,
+                          int n_weights, void *workspace, size_t workspace_bytes, void *stream);
+
 /* The same layer in two steps [SK "HQQLinear layer": the layer computes with the dequantized
  * weight]: given Wr, the binary16 weight [N, K] that hqq_dequantize wrote, Y[M, N] = X[M, K] .
  * Wr^T with binary32 sums (any order) rounded to binary16, on the matrix-core kernel of

@@ -222,3 +222,37 @@ def test_noalloc_rejects_before_any_device_call(H):
     big[1], big[2], big[3], big[5], big[11] = 8192, 8192, 4, 0, 16  # axis 0: ~156 MiB of scratch
     assert L.hqq_quantize_noalloc(*big) == 3
     assert "static scratch" in L.hqq_last_error().decode()
+
+
+def test_gemm_multi_validates(H):
+    """hqq_gemm_multi checks every weight before launching anything (fake device addresses:
+    a rejected call reaches no HIP call); errors name the weight; empty work is done."""
+    L = H.lib()
+    X, P, S, Z, Y, WS = (C.c_void_p(a) for a in (0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x8000))
+    ok, arg, uns, wsz = H.HQQ_OK, H.HQQ_ERR_ARG, H.HQQ_ERR_UNSUPPORTED, H.HQQ_ERR_WORKSPACE
+
+    def w(N=64, nbits=4, g=64, zb=16, meta=None, y=Y, packed=P):
+        return H.hqq_gemm_weight(packed, S, Z, meta, N, nbits, g, zb, y)
+
+    def gm(M, K, ws, n=None, work=None, wb=0):
+        arr = (H.hqq_gemm_weight * max(len(ws), 1))(*ws)
+        return L.hqq_gemm_multi(X, M, K, arr, len(ws) if n is None else n, work, wb, None)
+    assert gm(4, 128, []) == ok                                   # no weights
+    assert gm(0, 128, [w(), w(N=128)]) == ok                      # M = 0
+    assert gm(4, 128, [w(N=0)]) == ok                             # an empty weight
+    assert gm(-1, 128, [w()]) == arg
+    assert gm(4, 128, [w()], n=-1) == arg
+    assert L.hqq_gemm_multi(X, 4, 128, None, 2, None, 0, None) == arg
+    assert gm(4, 128, [w(), w(nbits=5)]) == arg
+    assert "weight 1" in H.hqq_last_error()
+    assert gm(4, 128, [w(g=8)]) == uns
+    assert gm(4, 100, [w()]) == arg                               # g | K
+    assert gm(4, 128, [w(), w(zb=12)]) == arg
+    assert gm(4, 128, [w(zb=8)]) == arg                           # 8-bit zeros need the meta
+    assert gm(4, 128, [w(), w(y=None)]) == arg
+    assert gm(4, 128, [w(y=C.c_void_p(0x5001))]) == arg           # Y 2-byte aligned
+    assert gm(4, 130, [w(nbits=3, g=10, packed=C.c_void_p(0x2002))]) != ok
+    big = L.hqq_gemm_workspace_bytes(100, 256, 128)
+    assert gm(100, 128, [w(N=64), w(N=256)], work=WS, wb=big - 1) == wsz   # the largest need
+    assert gm(100, 128, [w()], work=C.c_void_p(0x8008), wb=big) == arg     # 16-byte aligned
+    assert gm(1 << 30, 4096, [w()]) == arg                        # M*K too large

@@ -284,3 +284,53 @@ def test_gemm_f16_equals_workspace_path(O, dev, m, n, k):
     y1 = run_gemm(r, x16, m, n, k, nbits, g, zero_bits, dev, workspace=True)
     assert not np.isnan(y2).any()
     assert np.array_equal(y1, y2)
+
+
+def _random_weight(n, k, nbits, g, zero_bits, dev, gen, offset=0):
+    """A quantized weight with random codes, scales and zeros (every byte pattern is a valid
+    code stream): enough to compare two ways of multiplying it. `offset` shifts the packed
+    buffer off its allocation's alignment."""
+    nbytes = hqq.hqq_packed_bytes(n * k, nbits)
+    buf = torch.randint(0, 256, (nbytes + 16,), dtype=torch.uint8, device=dev, generator=gen)
+    ng = n * k // g
+    scale = (torch.rand(ng, device=dev, generator=gen) * 0.02 + 0.001).to(torch.float16)
+    if zero_bits == 16:
+        zero = (torch.rand(ng, device=dev, generator=gen) * 15).to(torch.float16)
+        meta = None
+    else:
+        zero = torch.randint(0, 256, (ng,), dtype=torch.uint8, device=dev, generator=gen)
+        meta = torch.tensor([0.0625, -1.5], dtype=torch.float16, device=dev)
+    return dict(packed=buf[offset:offset + nbytes], scale=scale, zero=zero, zero_meta=meta, N=n,
+                nbits=nbits, group_size=g, zero_bits=zero_bits)
+
+
+@pytest.mark.parametrize("m,workspace", [(1, False), (2, False), (5, False), (16, False),
+                                         (33, False), (64, False), (100, False), (100, True)])
+def test_gemm_multi_equals_single_calls(dev, m, workspace):
+    """hqq_gemm_multi writes, for every weight, exactly what hqq_gemm writes for it alone:
+    weights of several bit widths, group sizes and zero storages, ragged N, more weights than
+    one shared launch takes, and one packed buffer off its alignment (its own launch)."""
+    k = 1024
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77 + m)
+    specs = [(64, 4, 128, 8), (200, 4, 64, 16), (48, 2, 16, 8), (17, 8, 32, 16), (96, 3, 64, 8),
+             (100, 1, 128, 16)] + [(16 * (i + 1) + i, 4, 128, 8) for i in range(9)]
+    ws_ = [_random_weight(n, k, b, g, zb, dev, gen) for n, b, g, zb in specs]
+    ws_.append(_random_weight(40, k, 4, 64, 16, dev, gen, offset=1))
+    X = (torch.randn(m, k, device=dev, generator=gen) * 0.5).to(torch.float16)
+    work = None
+    if workspace:
+        wb = max(hqq.hqq_gemm_workspace_bytes(m, w["N"], k) for w in ws_)
+        work = torch.empty(wb, dtype=torch.uint8, device=dev)
+    for w in ws_:
+        w["Y"] = torch.full((m, w["N"]), float("nan"), dtype=torch.float16, device=dev)
+    print(f"multi m={m} workspace={workspace}: {len(ws_)} weights", flush=True)
+    hqq.hqq_gemm_multi(X, ws_, workspace=work)
+    torch.cuda.synchronize()
+    for i, w in enumerate(ws_):
+        single = torch.full_like(w["Y"], float("nan"))
+        hqq.hqq_gemm(X, w["packed"], w["scale"], w["zero"], w["zero_meta"], w["N"], k, w["nbits"],
+                     w["group_size"], w["zero_bits"], single, workspace=work)
+        torch.cuda.synchronize()
+        assert torch.equal(w["Y"].view(torch.int16), single.view(torch.int16)), \
+            f"weight {i} {specs[i] if i < len(specs) else 'unaligned'}"
