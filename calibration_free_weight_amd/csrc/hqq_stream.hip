@@ -1007,18 +1007,19 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 
             if (!idle) {
                 // ================= PASS: every lane with a group evaluates it ================
-                if (status == kActive) {
+                {
                     // Codes stay in range when the group's extreme weights do: u of the min (max)
                     // weight at least -1/2 (below 2^NBITS - 1/2). A binary32 bound that is off by
                     // its rounding puts that weight next to a rounding boundary, where the D test
                     // below hands the group to the exact path anyway. Groups that may clamp (about
-                    // one evaluation in 10^5) take the exact path.
+                    // one evaluation in 10^5) take the exact path. (Selects, not a branch: a join
+                    // here made the compiler copy the lane's state.)
                     const float ulo = fmaf(h2f(g_mnmx & 0xffffu), g_s, g_z);
                     const float uhi = fmaf(h2f(g_mnmx >> 16), g_s, g_z);
-                    if (!(ulo >= -0.5f && uhi < C::QMAX + 0.5f)) {
-                        g_meta = with_fl(g_meta, (meta_fl(g_meta) & (kSbExact | kFirst)) | (kDecide << 1));
-                        status = kHoldExq;
-                    }
+                    const bool clamp = status == kActive && !(ulo >= -0.5f && uhi < C::QMAX + 0.5f);
+                    g_meta = clamp ? with_fl(g_meta, (meta_fl(g_meta) & (kSbExact | kFirst)) | (kDecide << 1))
+                                   : g_meta;
+                    status = clamp ? (uint32_t)kHoldExq : status;
                 }
                 __builtin_amdgcn_s_setprio(0);
                 if (status == kActive) {
@@ -1030,50 +1031,53 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                         D = maxf_k<KP>(D);
                     }
                     const float Q = (float)rint(fma((double)G, (double)g_z, g_X) - (double)T);
+                    // The decision (the batch path's, written with selects: the branches of
+                    // the nested form made the compiler copy the lane's state at every join).
+                    // |S - S_exact| bounds: binary32 sums, G half-ulps of u plus the relative
+                    // summation error; the margins are far above the binary32 rounding of the
+                    // comparison itself.
                     const uint32_t fl = meta_fl(g_meta);
                     const bool first = fl & kFirst;
-                    bool accept = false;
-                    uint32_t next = kActive;
-                    if (D >= C::kThr) {
-                        g_meta = with_fl(g_meta, (fl & (kSbExact | kFirst)) | (kDecide << 1));
-                        next = kHoldExq;
-                    } else if (first || !a.early_stop) {
-                        accept = true;
-                    } else {
-                        // |S - S_exact| bounds (binary32 sums: G half-ulps of u plus the relative
-                        // summation error). The margins are far above the binary32 rounding of this
-                        // comparison itself.
-                        const float Sb = (float)g_Sb;
-                        const float m = (float)C::kElemErr + S * 0x1p-18f +
-                                        ((fl & kSbExact) ? 0x1p-18f * Sb
-                                                           : 4.0f * (float)C::kElemErr + Sb * 0x1p-18f);
-                        if (S > Sb + m) next = kHoldFin;
-                        else if (S < Sb - m) accept = true;
-                        else {
-                            g_meta = with_fl(g_meta, (fl & kSbExact) | (kDecide << 1));
-                            next = kHoldExq;
-                        }
+                    const float Sb = (float)g_Sb;
+                    const float m = (float)C::kElemErr + S * 0x1p-18f +
+                                    ((fl & kSbExact) ? 0x1p-18f * Sb
+                                                       : 4.0f * (float)C::kElemErr + Sb * 0x1p-18f);
+                    const bool guard = D >= C::kThr;                  // to the exact path
+                    const bool plain = first || !a.early_stop;        // accepted unseen
+                    const bool rise = !guard && !plain && S > Sb + m; // stop: the error rose
+                    const bool accept = !guard && (plain || S < Sb - m);
+                    const bool undecided = !guard && !plain && !rise && !accept;
+                    // advance of an accepted evaluation (advance_core's steps with zb = z)
+                    const int t = (int)meta_t(g_meta);
+                    const bool over = t > a.iters;
+                    const float dmax = D + (0.5f - C::kThr);
+                    const bool dead_all = dmax <= tau_min * g_s;
+                    bool live = false;                                // the shrink is live
+                    if (accept && !over && !dead_all) {
+                        const float tau_t = (float)pow_ool((double)g_beta, tau_exp);
+                        live = !(dmax <= tau_t * (g_s * (1.0f - 4e-6f)));
                     }
-                    if (accept) {
-                        g_zb = g_z;
-                        g_Sb = S;
-                        g_Db = D;
-                        g_meta = with_fl(g_meta, 0);
-                        const Advance ad = advance_core<C>((int)meta_t(g_meta), a.iters, g_s, g_z, Q, D,
-                                                                  false, g_X, g_beta, tau_min,
-                                                                  tau_exp);
-                        if (ad.out == kDone) {
-                            g_zb = ad.zn;
-                            next = kHoldFin;
-                        } else if (ad.out == kNeedShrink) {
-                            g_meta = with_fl(g_meta, kShrink << 1);
-                            next = kHoldExq;
-                        } else {
-                            g_z = ad.zn;
-                            g_beta = g_beta * a.kappa;
-                            g_meta = g_meta + (1u << 8);
-                        }
-                    }
+                    const float zn = (float)(((double)Q - g_X) * (1.0 / G));
+                    const bool fixed = !over && !live && zn == g_z && dead_all;
+                    const bool fin = accept && (over || fixed);
+                    const bool nxt = accept && !over && !live && !fixed;
+                    const bool shr = accept && live;
+                    const uint32_t acc_meta = with_fl(g_meta, 0);
+                    uint32_t meta = g_meta;
+                    meta = guard ? with_fl(g_meta, (fl & (kSbExact | kFirst)) | (kDecide << 1)) : meta;
+                    meta = undecided ? with_fl(g_meta, (fl & kSbExact) | (kDecide << 1)) : meta;
+                    meta = fin ? acc_meta : meta;
+                    meta = shr ? with_fl(acc_meta, kShrink << 1) : meta;
+                    meta = nxt ? acc_meta + (1u << 8) : meta;
+                    g_meta = meta;
+                    g_zb = accept ? (fixed ? zn : g_z) : g_zb;
+                    g_Sb = accept ? (double)S : g_Sb;
+                    g_Db = accept ? D : g_Db;
+                    g_beta = nxt ? g_beta * a.kappa : g_beta;
+                    g_z = nxt ? zn : g_z;
+                    const uint32_t next = (guard || undecided || shr) ? kHoldExq
+                                          : (rise || fin)            ? kHoldFin
+                                                                     : kActive;
                     status = next;
                 }
                 continue;
@@ -1237,11 +1241,12 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
             ran_out = true;
             break;
         }
-        if (step == kStepFast) {
+        {
             const float ulo = fmaf(umn, s, z), uhi = fmaf(umx, s, z);
-            if (!(ulo >= -0.5f && uhi < C::QMAX + 0.5f)) step = kStepExact;   // may clamp
+            const bool clamp = step == kStepFast && !(ulo >= -0.5f && uhi < C::QMAX + 0.5f);
+            step = clamp ? (uint8_t)kStepExact : step;           // may clamp
         }
-        // ---- binary32 evaluation ----
+        // ---- binary32 evaluation; the decision as in the persistent kernel, with selects ----
         if (step == kStepFast) {
             float S, T, D;
             eval_fast<NBITS, WB>(xb, s, z, S, T, D);
@@ -1251,41 +1256,38 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
                 D = maxf_k<KB>(D);
             }
             const float Q = (float)rint(fma((double)G, (double)z, X) - (double)T);
-            bool accept = false;
-            if (D >= C::kThr) {
-                step = kStepExact;
-            } else if (first || !a.early_stop) {
-                accept = true;
-            } else {
-                const float Sb32 = (float)Sb;
-                const float m = (float)C::kElemErr + S * 0x1p-18f +
-                                (sbexact ? 0x1p-18f * Sb32 : 4.0f * (float)C::kElemErr + Sb32 * 0x1p-18f);
-                if (S > Sb32 + m) step = kStepDone;
-                else if (S < Sb32 - m) accept = true;
-                else {
-                    first = false;
-                    step = kStepExact;
-                }
+            const float Sb32 = (float)Sb;
+            const float m = (float)C::kElemErr + S * 0x1p-18f +
+                            (sbexact ? 0x1p-18f * Sb32 : 4.0f * (float)C::kElemErr + Sb32 * 0x1p-18f);
+            const bool guard = D >= C::kThr;
+            const bool plain = first || !a.early_stop;
+            const bool rise = !guard && !plain && S > Sb32 + m;
+            const bool accept = !guard && (plain || S < Sb32 - m);
+            const bool undecided = !guard && !plain && !rise && !accept;
+            const bool over = t > a.iters;
+            const float dmax = D + (0.5f - C::kThr);
+            const bool dead_all = dmax <= tau_min * s;
+            bool live = false;
+            if (accept && !over && !dead_all) {
+                const float tau_t = (float)pow_ool((double)beta, tau_exp);
+                live = !(dmax <= tau_t * (s * (1.0f - 4e-6f)));
             }
-            if (accept) {
-                zb = z;
-                Sb = S;
-                Db = D;
-                first = false;
-                sbexact = false;
-                const Advance ad = advance_core<C>(t, a.iters, s, z, Q, D, false, X, beta,
-                                                   tau_min, tau_exp);
-                if (ad.out == kDone) {
-                    zb = ad.zn;
-                    step = kStepDone;
-                } else if (ad.out == kNeedShrink) {
-                    step = kStepShrink;
-                } else {
-                    z = ad.zn;
-                    beta = beta * a.kappa;
-                    ++t;
-                }
-            }
+            const float zn = (float)(((double)Q - X) * (1.0 / G));
+            const bool fixed = !over && !live && zn == z && dead_all;
+            const bool fin = accept && (over || fixed);
+            const bool nxt = accept && !over && !live && !fixed;
+            zb = accept ? (fixed ? zn : z) : zb;
+            Sb = accept ? (double)S : Sb;
+            Db = accept ? D : Db;
+            first = (accept || undecided) ? false : first;
+            sbexact = accept ? false : sbexact;
+            beta = nxt ? beta * a.kappa : beta;
+            t = nxt ? t + 1 : t;
+            z = nxt ? zn : z;
+            step = (guard || undecided) ? (uint8_t)kStepExact
+                   : (rise || fin)      ? (uint8_t)kStepDone
+                   : (accept && live)   ? (uint8_t)kStepShrink
+                                        : step;
         }
         // ---- exact decision (binary64), for the groups the fast path could not settle ----
         if (__ballot(step == kStepExact)) {
