@@ -1022,7 +1022,12 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                     status = clamp ? (uint32_t)kHoldExq : status;
                 }
                 __builtin_amdgcn_s_setprio(0);
-                if (status == kActive) {
+                {
+                    // Every lane runs the evaluation (the wave issues it for its active lanes
+                    // anyway); lanes without an active group keep their state through the
+                    // selects below. A branch here made the compiler keep the lane's state in
+                    // two register sets and copy between them on every loop turn.
+                    const bool act = status == kActive;
                     float S, T, D;
                     eval_fast<NBITS, WP>(xr, g_s, g_z, S, T, D);
                     if (KP > 1) {              // butterflies: every lane of the group gets
@@ -1042,11 +1047,11 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                     const float m = (float)C::kElemErr + S * 0x1p-18f +
                                     ((fl & kSbExact) ? 0x1p-18f * Sb
                                                        : 4.0f * (float)C::kElemErr + Sb * 0x1p-18f);
-                    const bool guard = D >= C::kThr;                  // to the exact path
+                    const bool guard = act && D >= C::kThr;           // to the exact path
                     const bool plain = first || !a.early_stop;        // accepted unseen
-                    const bool rise = !guard && !plain && S > Sb + m; // stop: the error rose
-                    const bool accept = !guard && (plain || S < Sb - m);
-                    const bool undecided = !guard && !plain && !rise && !accept;
+                    const bool rise = act && !guard && !plain && S > Sb + m;   // the error rose
+                    const bool accept = act && !guard && (plain || S < Sb - m);
+                    const bool undecided = act && !guard && !plain && !rise && !accept;
                     // advance of an accepted evaluation (advance_core's steps with zb = z)
                     const int t = (int)meta_t(g_meta);
                     const bool over = t > a.iters;
@@ -1075,10 +1080,9 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                     g_Db = accept ? D : g_Db;
                     g_beta = nxt ? g_beta * a.kappa : g_beta;
                     g_z = nxt ? zn : g_z;
-                    const uint32_t next = (guard || undecided || shr) ? kHoldExq
-                                          : (rise || fin)            ? kHoldFin
-                                                                     : kActive;
-                    status = next;
+                    status = (guard || undecided || shr) ? (uint32_t)kHoldExq
+                             : (rise || fin)              ? (uint32_t)kHoldFin
+                                                          : status;
                 }
                 continue;
             }
