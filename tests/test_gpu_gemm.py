@@ -112,11 +112,12 @@ def test_gemm_decode_ragged(O, dev, nbits, g, zero_bits):
                 check(O, r, x16, y, m, n, k, g, zero_bits, label)
 
 
-@pytest.mark.parametrize("nbits,g,zero_bits", [(4, 16, 8), (3, 32, 16), (8, 16, 16), (1, 64, 8)])
+@pytest.mark.parametrize("nbits,g,zero_bits", [(4, 16, 8), (3, 32, 16), (8, 16, 16), (1, 64, 8),
+                                               (4, 64, 16), (8, 64, 8), (4, 32, 8)])
 def test_gemm_skinny_ragged(O, dev, nbits, g, zero_bits):
     # the matrix-core skinny kernel (8 < M <= 64): one to four 16-row M tiles, N below, at and
-    # past one 16-row block, K of one 32-wide step (three of the block's four waves idle),
-    # a few steps, and a half step at the end
+    # past one 16-row block, K of one 32-wide step (most of the block's waves idle), a few
+    # steps, and a half step at the end
     for m in (9, 17, 33, 48, 64):
         for n, k in ((15, g), (16, 3 * g), (17, 64 + g), (200, 4096 + g)):
             label = f"skinny m={m} n={n} k={k} nbits={nbits} g={g} zb={zero_bits}"
