@@ -751,7 +751,10 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
     // A bound on loop steps that the schedule never reaches (every step moves at least one
     // group forward): a defect ends the launch instead of hanging it, and the wave that runs
     // out sets the launch's status flag so that the host can report incomplete outputs.
-    int64_t budget = a.budget0;
+    // 32-bit (scalar compares; the host's budgets stay far below 2^31 per wave, and the
+    // per-tile additions saturate).
+    int32_t budget = (int32_t)(a.budget0 < 0x40000000 ? a.budget0 : 0x40000000);
+    const int32_t budget_tile = (int32_t)(a.budget_tile < 0x40000000 ? a.budget_tile : 0x40000000);
     bool ran_out = false;
 
     prefetch();
@@ -782,9 +785,11 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             // one and the free slots take the tile and every holder that needs a free slot
             // (with in-place swaps, those the ready groups and the tile's cannot take): one
             // swap then serves them all.
+            // (fre_n >= GB + max(n_hold - partners, 0), written without a saturating
+            // subtraction, which has only a vector form)
             const uint32_t partners = C::XCHG ? rdy_n + GB : 0u;
             if (pf_ok && rdy_n < n_empty + n_hold &&
-                fre_n >= GB + (n_hold > partners ? n_hold - partners : 0u))
+                fre_n + (n_hold < partners ? n_hold : partners) >= GB + n_hold)
                 break;   // INIT
 
             if ((n_hold > 0 && (rdy_n > 0 || fre_n > 0)) || (n_empty > 0 && rdy_n > 0)) {
@@ -1103,7 +1108,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
         }
         // ================= INIT: a prefetched tile becomes ready groups ===============
         __builtin_amdgcn_s_setprio(0);
-        budget += a.budget_tile;
+        budget = budget > 0x7fffffff - budget_tile ? 0x7fffffff : budget + budget_tile;
         const int nv = pf_nv;
         const bool valid = k < nv;
         uint8_t j = 0;
@@ -1154,15 +1159,21 @@ __device__ __forceinline__ Exact eval_exact_regs(const uint32_t (&xb)[C::WB], fl
 {
     const double sd = s, zd = z, qm = C::QMAX;
     double s_ = 0.0, q_ = 0.0, d_ = 0.0;
+    // two words (four weights) per turn: a register array indexed in a rolled loop costs an
+    // indexed move per index, and the binary64 sums are exact in any order
 #pragma unroll 1
-    for (int i = 0; i < C::EB; ++i) {
-        const uint32_t h = i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu;
-        const double u = fma((double)h2f(h), sd, zd);
-        const double c = fmin(fmax(rint(u), 0.0), qm);
-        const double e = fabs(u - c);
-        s_ += e;
-        q_ += c;
-        d_ = fmax(d_, e);
+    for (int w = 0; w < C::WB; w += 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t v = xb[w + (i >> 1)];
+            const uint32_t h = i & 1 ? v >> 16 : v & 0xffffu;
+            const double u = fma((double)h2f(h), sd, zd);
+            const double c = fmin(fmax(rint(u), 0.0), qm);
+            const double e = fabs(u - c);
+            s_ += e;
+            q_ += c;
+            d_ = fmax(d_, e);
+        }
     }
     return Exact{s_, q_, d_};
 }
