@@ -350,20 +350,27 @@ struct Exact {
 };
 
 // Exact (binary64) evaluation of one batch lane's EB weights (chunks c0.. of slot j) at zero
-// z. Rare: a rolled loop, so it adds few registers to the binary32 path.
+// z. Rare: a rolled loop over the 16-byte chunks (one LDS read each), so it adds few
+// registers to the binary32 path; the binary64 sums are exact in any order.
 template <class C>
 __device__ __forceinline__ Exact eval_exact(const uint16_t *xs, int j, int c0, float s, float z)
 {
     const double sd = s, zd = z, qm = C::QMAX;
     double s_ = 0.0, q_ = 0.0, d_ = 0.0;
 #pragma unroll 1
-    for (int i = 0; i < C::EB; ++i) {
-        const double u = fma((double)h2f(xs[chunk_at<C::CS>(j, c0 + (i >> 3)) + (i & 7)]), sd, zd);
-        const double c = fmin(fmax(rint(u), 0.0), qm);
-        const double e = fabs(u - c);
-        s_ += e;
-        q_ += c;
-        d_ = fmax(d_, e);
+    for (int c = 0; c < C::EB / 8; ++c) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(j, c0 + c));
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t h = i & 1 ? w4[i >> 1] >> 16 : w4[i >> 1] & 0xffffu;
+            const double u = fma((double)h2f(h), sd, zd);
+            const double c2 = fmin(fmax(rint(u), 0.0), qm);
+            const double e = fabs(u - c2);
+            s_ += e;
+            q_ += c2;
+            d_ = fmax(d_, e);
+        }
     }
     return Exact{s_, q_, d_};
 }
@@ -1344,12 +1351,16 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
                 const double zd = zb, qm = C::QMAX, bd = beta;
                 double acc = 0.0;
 #pragma unroll 1
-                for (int i = 0; i < EB; ++i) {
-                    const double xv = h2f(i & 1 ? xb[i >> 1] >> 16 : xb[i >> 1] & 0xffffu);
-                    const double u = fma(xv, sd, zd);
-                    const double c = fmin(fmax(rint(u), 0.0), qm);
-                    const double we = shrink((u - c) / sd, pm1, bd);
-                    acc += c - (xv - we) * sd;
+                for (int w = 0; w < WB; w += 2) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t v = xb[w + (i >> 1)];
+                        const double xv = h2f(i & 1 ? v >> 16 : v & 0xffffu);
+                        const double u = fma(xv, sd, zd);
+                        const double c = fmin(fmax(rint(u), 0.0), qm);
+                        const double we = shrink((u - c) / sd, pm1, bd);
+                        acc += c - (xv - we) * sd;
+                    }
                 }
                 acc = addd_k<KB>(acc);
                 z = (float)(acc * (1.0 / G));
