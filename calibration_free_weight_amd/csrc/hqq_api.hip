@@ -702,10 +702,10 @@ hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *sc
     if (M > 0 && K > (int64_t(1) << 40) / M) return fail(HQQ_ERR_ARG, "M*K too large");
     if (zero_bits != 8 && zero_bits != 16) return fail(HQQ_ERR_ARG, "zero_bits must be 8 or 16");
     if (M == 0 || N == 0) return HQQ_OK;
-    if (!X) return fail(HQQ_ERR_ARG, "X, Y, packed, scale and zero must be non-null");
+    if (!X && K > 0) return fail(HQQ_ERR_ARG, "X, Y, packed, scale and zero must be non-null");
     st = check_gemm_weight(packed, scale, zero, zero_meta, N, K, nbits, group_size, zero_bits, Y, "");
     if (st != HQQ_OK) return st;
-    if (!aligned(X, 16)) return fail(HQQ_ERR_ARG, "X must be 16-byte aligned");
+    if (K > 0 && !aligned(X, 16)) return fail(HQQ_ERR_ARG, "X must be 16-byte aligned");
     const size_t need = hqq::gemm_workspace_bytes(M, N, K);
     if (workspace && need > 0 && workspace_bytes < need)
         return fail(HQQ_ERR_WORKSPACE, "workspace smaller than hqq_gemm_workspace_bytes(M, N, K)");
@@ -753,8 +753,8 @@ hqq_status hqq_gemm_multi(const void *X, int64_t M, int64_t K, const hqq_gemm_we
         g_last_error.clear();
         return HQQ_OK;
     }
-    if (!X) return fail(HQQ_ERR_ARG, "X must be non-null");
-    if (!aligned(X, 16)) return fail(HQQ_ERR_ARG, "X must be 16-byte aligned");
+    if (!X && K > 0) return fail(HQQ_ERR_ARG, "X must be non-null");
+    if (K > 0 && !aligned(X, 16)) return fail(HQQ_ERR_ARG, "X must be 16-byte aligned");
     if (workspace && need > 0 && workspace_bytes < need)
         return fail(HQQ_ERR_WORKSPACE,
                     "workspace smaller than the largest hqq_gemm_workspace_bytes(M, N_i, K)");

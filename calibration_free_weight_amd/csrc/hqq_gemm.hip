@@ -1212,12 +1212,37 @@ hipError_t launch_gemm_f16(const uint16_t *X, int64_t M, const uint16_t *Wr, int
     return hipGetLastError();
 }
 
+namespace {
+
+// Y = 0 for an empty sum (K = 0): the weight buffers may be empty or null then, so no
+// multiplying kernel may run (a fill kernel rather than a memset, so that the call can be
+// captured into a graph).
+__global__ void __launch_bounds__(256) zero_kernel(uint16_t *__restrict__ Y, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        Y[i] = 0;
+}
+
+void launch_zero(uint16_t *Y, int64_t n, hipStream_t stream)
+{
+    if (n <= 0) return;
+    int64_t b = (n + 255) / 256;
+    if (b > 4096) b = 4096;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)b), dim3(256), 0, stream, Y, n);
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const uint16_t *X, int64_t M, const uint8_t *packed, const uint16_t *scale,
                        const void *zero, const uint16_t *zero_meta, int64_t N, int64_t K,
                        int nbits, int g, int zero_bits, uint16_t *Y, uint16_t *Wr,
                        hipStream_t stream)
 {
     if (M == 0 || N == 0) return hipSuccess;
+    if (K == 0) {
+        launch_zero(Y, M * N, stream);
+        return hipGetLastError();
+    }
     int lg = 0;
     while ((1 << lg) < g) ++lg;
     const QW w{packed, scale, zero, zero_bits == 8 ? zero_meta : nullptr, N, K, lg, zero_bits};
@@ -1250,6 +1275,12 @@ hipError_t launch_gemm_multi(const uint16_t *X, int64_t M, int64_t K, const Gemm
         }
         if (w.empty()) continue;
         const int m = (int)w.size();
+        if (K == 0) {
+            for (int i = 0; i < m; ++i) launch_zero(Y[i], M * w[i].N, stream);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            continue;
+        }
         switch (nbits) {
         case 1: launch_nb<1>(X, M, w.data(), Y.data(), m, Wr, stream); break;
         case 2: launch_nb<2>(X, M, w.data(), Y.data(), m, Wr, stream); break;

@@ -227,7 +227,9 @@ hqq_status hqq_dequantize_scales(const uint8_t *scale_q, const void *scale_meta,
  * binary16 matrix-core GEMM reads it (the faster choice for large M); NULL keeps the
  * streaming kernels. A non-NULL workspace that is too small is HQQ_ERR_WORKSPACE. Its
  * contents are scratch; calls that share one race. Packed buffers that are not 4-byte
- * aligned (8 bytes at 8 bits) take slower fallback kernels, with or without a workspace. */
+ * aligned (8 bytes at 8 bits) take slower fallback kernels, with or without a workspace.
+ * K = 0 (an empty sum) writes Y = 0; X, packed, scale, zero and zero_meta may then be NULL.
+ * M = 0 or N = 0 does nothing. */
 hqq_status hqq_gemm(const void *X, int64_t M, const void *packed, const void *scale,
                     const void *zero, const void *zero_meta, int64_t N, int64_t K, int nbits,
                     int group_size, int zero_bits, void *Y, void *workspace,
@@ -258,7 +260,8 @@ typedef struct hqq_gemm_weight {
  * attention block's q, k and v projections, or an MLP's gate and up projections, fill the
  * GPU together rather than one after another; the others are launched one by one. Every
  * weight is [N_i, K] with the same K; X as in hqq_gemm; the Y_i must not overlap each other
- * or X. n_weights = 0, M = 0 or N_i = 0 do nothing for those weights. workspace: as in
+ * or X. n_weights = 0, M = 0 or N_i = 0 do nothing for those weights; K = 0 writes Y_i = 0
+ * (X and the weight buffers may then be NULL). workspace: as in
  * hqq_gemm, at least the largest hqq_gemm_workspace_bytes(M, N_i, K), used by one weight
  * after another; too small is HQQ_ERR_WORKSPACE. Argument errors name the weight; nothing is
  * launched when any weight is invalid. Nothing is allocated on the device. */

@@ -335,3 +335,26 @@ def test_gemm_multi_equals_single_calls(dev, m, workspace):
         torch.cuda.synchronize()
         assert torch.equal(w["Y"].view(torch.int16), single.view(torch.int16)), \
             f"weight {i} {specs[i] if i < len(specs) else 'unaligned'}"
+
+
+def test_gemm_empty_k_writes_zeros(dev):
+    # K = 0 is an empty sum: Y = 0 on every path (decode, skinny, sliced and workspace M), and
+    # neither X nor the weight buffers are read, so they may be null
+    nan = float("nan")
+    for m in (1, 5, 64, 100):
+        for nbits, zb in ((4, 8), (3, 16), (2, 16)):
+            label = f"empty K m={m} nbits={nbits} zb={zb}"
+            print(label, flush=True)
+            X = torch.empty((m, 0), dtype=torch.float16, device=dev)
+            Y = torch.full((m, 37), nan, dtype=torch.float16, device=dev)
+            ws = torch.zeros(256, dtype=torch.uint8, device=dev) if m > 64 else None
+            hqq.hqq_gemm(X, None, None, None, None, 37, 0, nbits, 64, zb, Y, workspace=ws)
+            torch.cuda.synchronize()
+            assert bool((Y == 0).all()), label
+    X = torch.empty((7, 0), dtype=torch.float16, device=dev)
+    Ys = [torch.full((7, n), nan, dtype=torch.float16, device=dev) for n in (16, 33, 5)]
+    hqq.hqq_gemm_multi(X, [dict(packed=None, scale=None, zero=None, zero_meta=None, N=Y.shape[1],
+                                nbits=nb, group_size=128, zero_bits=16, Y=Y)
+                           for Y, nb in zip(Ys, (4, 4, 8))])
+    torch.cuda.synchronize()
+    assert all(bool((Y == 0).all()) for Y in Ys)
