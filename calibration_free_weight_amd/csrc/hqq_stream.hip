@@ -1185,6 +1185,35 @@ __device__ __forceinline__ Exact eval_exact_regs(const uint32_t (&xb)[C::WB], fl
     return Exact{s_, q_, d_};
 }
 
+// eval_exact_regs at z, and in the same loop the exact error sum at a second zero zb (each
+// sum in the same order as eval_exact_regs would take it).
+template <class C>
+__device__ __forceinline__ Exact eval_exact2_regs(const uint32_t (&xb)[C::WB], float s, float z,
+                                                  float zb, double &Sb_out)
+{
+    const double sd = s, zd = z, zbd = zb, qm = C::QMAX;
+    double s_ = 0.0, q_ = 0.0, d_ = 0.0, sb_ = 0.0;
+#pragma unroll 1
+    for (int w = 0; w < C::WB; w += 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t v = xb[w + (i >> 1)];
+            const double x = (double)h2f(i & 1 ? v >> 16 : v & 0xffffu);
+            const double u = fma(x, sd, zd);
+            const double c = fmin(fmax(rint(u), 0.0), qm);
+            const double e = fabs(u - c);
+            s_ += e;
+            q_ += c;
+            d_ = fmax(d_, e);
+            const double ub = fma(x, sd, zbd);
+            const double cb = fmin(fmax(rint(ub), 0.0), qm);
+            sb_ += fabs(ub - cb);
+        }
+    }
+    Sb_out = sb_;
+    return Exact{s_, q_, d_};
+}
+
 // Lockstep solver for classes too small to keep the persistent waves busy (a single layer,
 // say). One wave per tile of GB groups in the batch layout (KB lanes per group, EB weights
 // per lane, held in registers): every group of the tile is iterated in place, each loop turn
@@ -1313,13 +1342,18 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
         }
         // ---- exact decision (binary64), for the groups the fast path could not settle ----
         if (__ballot(step == kStepExact)) {
+            // the accepted error is re-evaluated exactly when the fast path accepted it: in
+            // the same loop over the weights as the candidate's when any group needs it
+            const bool any_sbx = __ballot(step == kStepExact && !first && !sbexact) != 0;
             if (step == kStepExact) {
-                const Exact xn = eval_exact_regs<C>(xb, s, z);
+                double sbx_l = 0.0;
+                const Exact xn = any_sbx ? eval_exact2_regs<C>(xb, s, z, zb, sbx_l)
+                                         : eval_exact_regs<C>(xb, s, z);
                 const double S = addd_k<KB>(xn.S);
                 const float Q = (float)addd_k<KB>(xn.Q);
                 const float D = maxf_k<KB>((float)xn.D);
                 double Sbx = Sb;
-                if (!first && !sbexact) Sbx = addd_k<KB>(eval_exact_regs<C>(xb, s, zb).S);
+                if (!first && !sbexact) Sbx = addd_k<KB>(sbx_l);
                 if (first || !a.early_stop || S <= Sbx) {
                     zb = z;
                     Db = D;
