@@ -183,6 +183,18 @@ __device__ __forceinline__ double lane_sum_xs(const uint32_t (&xb)[W], double sd
     }
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
+// Another lane's value (ds_bpermute from lane src), binary32 or binary64.
+__device__ __forceinline__ float bperm_f(int src, float v)
+{
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+__device__ __forceinline__ double bperm_d(int src, double v)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)(b >> 32));
+    return __longlong_as_double((long long)((uint64_t)hi << 32 | lo));
+}
 // LDS atomic swap of 8 bytes (ds_wrxchg_rtn_b64): stores v, returns the old contents.
 __device__ __forceinline__ uint64_t xchg_l(uint64_t *p, uint64_t v)
 {
@@ -1230,6 +1242,7 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
     using C = Cfg<NBITS, G>;
     constexpr int EB = C::EB, KB = C::KB, GB = C::GB, WB = C::WB;
     __shared__ __attribute__((aligned(4))) uint8_t stage[NBITS == 3 ? 64 * EB : 4];
+    __shared__ __attribute__((aligned(16))) uint32_t xl[64 * WB];   // the wave's weights (exact turns)
     const int lane = threadIdx.x;
     const int k = lane / KB, sub = lane % KB;
     const bool bleader = sub == 0;
@@ -1287,6 +1300,32 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
     int64_t budget = a.budget0 + a.budget_tile;
     bool ran_out = false;
 
+    // the decision after an exact evaluation (S, Q, D at z; Sbx the accepted error)
+    auto exact_decide = [&](double S, float Q, float D, double Sbx) {
+        if (first || !a.early_stop || S <= Sbx) {
+            zb = z;
+            Db = D;
+            Sb = S;
+            first = false;
+            sbexact = true;
+            const Advance ad = advance_core<C>(t, a.iters, s, z, Q, D, true, X, beta, tau_min,
+                                               tau_exp);
+            if (ad.out == kDone) {
+                zb = ad.zn;
+                step = kStepDone;
+            } else if (ad.out == kNeedShrink) {
+                step = kStepShrink;
+            } else {
+                z = ad.zn;
+                beta = beta * a.kappa;
+                ++t;
+                step = kStepFast;
+            }
+        } else {
+            step = kStepDone;
+        }
+    };
+
     while (__ballot(step != kStepDone)) {
         if (--budget <= 0) {
             ran_out = true;
@@ -1340,42 +1379,85 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
                    : (accept && live)   ? (uint8_t)kStepShrink
                                         : step;
         }
-        // ---- exact decision (binary64), for the groups the fast path could not settle ----
-        if (__ballot(step == kStepExact)) {
-            // the accepted error is re-evaluated exactly when the fast path accepted it: in
-            // the same loop over the weights as the candidate's when any group needs it
+        // ---- exact decision (binary64), for the groups the fast path could not settle; the
+        //      accepted error is re-evaluated exactly (at zb) when the fast path accepted it.
+        //      A group held by one lane (g16, g32) sums its errors element by element, in the
+        //      oracle's order, which fixes the result even where a sum rounds.
+        if (KB == 1 && __ballot(step == kStepExact)) {
             const bool any_sbx = __ballot(step == kStepExact && !first && !sbexact) != 0;
             if (step == kStepExact) {
                 double sbx_l = 0.0;
                 const Exact xn = any_sbx ? eval_exact2_regs<C>(xb, s, z, zb, sbx_l)
                                          : eval_exact_regs<C>(xb, s, z);
-                const double S = addd_k<KB>(xn.S);
-                const float Q = (float)addd_k<KB>(xn.Q);
-                const float D = maxf_k<KB>((float)xn.D);
                 double Sbx = Sb;
-                if (!first && !sbexact) Sbx = addd_k<KB>(sbx_l);
-                if (first || !a.early_stop || S <= Sbx) {
-                    zb = z;
-                    Db = D;
-                    Sb = S;
-                    first = false;
-                    sbexact = true;
-                    const Advance ad = advance_core<C>(t, a.iters, s, z, Q, D, true, X, beta,
-                                                       tau_min, tau_exp);
-                    if (ad.out == kDone) {
-                        zb = ad.zn;
-                        step = kStepDone;
-                    } else if (ad.out == kNeedShrink) {
-                        step = kStepShrink;
-                    } else {
-                        z = ad.zn;
-                        beta = beta * a.kappa;
-                        ++t;
-                        step = kStepFast;
-                    }
-                } else {
-                    step = kStepDone;
+                if (!first && !sbexact) Sbx = sbx_l;
+                exact_decide(xn.S, (float)xn.Q, (float)xn.D, Sbx);
+            }
+        } else if (KB > 1 && __ballot(step == kStepExact)) {
+            // A group spread over several lanes already sums in another order than the
+            // oracle's, relying on the sums being exact (they are unless a group's range is
+            // extreme, the oracle's own precision reading). A turn has few such groups, so
+            // their weights are spread over the whole wave first (through LDS; LPG lanes of
+            // four weights per group, NPC groups per round): the binary64 loop then takes
+            // four weights per lane instead of EB.
+            constexpr int LPG = G / 4, NPC = 64 / LPG;
+            const bool any_sbx = __ballot(step == kStepExact && !first && !sbexact) != 0;
+#pragma unroll
+            for (int i = 0; i < WB / 4; ++i)
+                *reinterpret_cast<u32x4 *>(xl + lane * WB + 4 * i) =
+                    u32x4{xb[4 * i], xb[4 * i + 1], xb[4 * i + 2], xb[4 * i + 3]};
+            __syncthreads();
+            const int slot = lane / LPG, part = lane % LPG;
+            uint64_t m_left = __ballot(step == kStepExact && bleader);
+            while (m_left) {
+                // this round: the next NPC waiting groups; slot q holds the q-th (leader lane L)
+                uint64_t m_round = 0;
+                int lead = 0;
+                for (int q = 0; q < NPC && m_left; ++q) {
+                    const int L = __builtin_ctzll(m_left);
+                    m_left &= m_left - 1;
+                    m_round |= 1ull << L;
+                    lead = slot == q ? L : lead;
                 }
+                // the slot's group: s and zeros from its leader, four weights from LDS (group g
+                // sits at words g*G/2 = L*WB; slots without a group compute unused values)
+                const double sd = bperm_f(lead, s), zd = bperm_f(lead, z), zbd = bperm_f(lead, zb);
+                const double qm = C::QMAX;
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(xl + lead * WB + 2 * part);
+                double se = 0.0, qe = 0.0, de = 0.0, sbe = 0.0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = e < 2 ? v.x : v.y;
+                    const double x = (double)h2f(e & 1 ? w >> 16 : w & 0xffffu);
+                    const double u = fma(x, sd, zd);
+                    const double c = fmin(fmax(rint(u), 0.0), qm);
+                    const double d = fabs(u - c);
+                    se += d;
+                    qe += c;
+                    de = fmax(de, d);
+                    if (any_sbx) {
+                        const double ub = fma(x, sd, zbd);
+                        const double cb = fmin(fmax(rint(ub), 0.0), qm);
+                        sbe += fabs(ub - cb);
+                    }
+                }
+                se = addd_k<LPG>(se);
+                qe = addd_k<LPG>(qe);
+                const float dm = maxf_k<LPG>((float)de);
+                if (any_sbx) sbe = addd_k<LPG>(sbe);
+                // back to the lanes of each group of the round (every lane of a slot holds the
+                // sums)
+                const int my_lead = lane - sub;
+                const bool mine = step == kStepExact && ((m_round >> my_lead) & 1ull);
+                const int src = __builtin_popcountll(m_round & ((1ull << my_lead) - 1ull)) * LPG;
+                const double S = bperm_d(src, se);
+                const float Q = (float)bperm_d(src, qe);
+                const float D = bperm_f(src, dm);
+                const double Sbe = any_sbx ? bperm_d(src, sbe) : 0.0;
+                if (!mine) continue;
+                double Sbx = Sb;
+                if (!first && !sbexact) Sbx = Sbe;
+                exact_decide(S, Q, D, Sbx);
             }
         }
         // ---- zero update with the shrink live: z = mean(q - (x - W_e)*s), W_e from the
