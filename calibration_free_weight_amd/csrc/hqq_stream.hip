@@ -195,6 +195,22 @@ __device__ __forceinline__ double bperm_d(int src, double v)
     const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)(b >> 32));
     return __longlong_as_double((long long)((uint64_t)hi << 32 | lo));
 }
+// Sum of a lane's E weights in binary64, for groups whose weights are all below 1/2 in
+// magnitude: each binary16 pair is added by v_dot2 against {1, 1}, exactly (a multiple of 2^-24
+// below 1 fits binary32; checked on every pattern class, subnormals included), and the pair
+// sums add exactly in binary64 (below 2^23 units of 2^-24). s * (this sum) then rounds the
+// exact sum x*s once, so it equals lane_sum_xs's result wherever that one is exact.
+template <int W>
+__device__ __forceinline__ double lane_sum_x(const uint32_t (&xb)[W])
+{
+    typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
+    const hh2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+        acc[i & 3] += (double)__builtin_amdgcn_fdot2(__builtin_bit_cast(hh2, xb[i]), one, 0.0f, false);
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
 // LDS atomic swap of 8 bytes (ds_wrxchg_rtn_b64): stores v, returns the old contents.
 __device__ __forceinline__ uint64_t xchg_l(uint64_t *p, uint64_t v)
 {
@@ -1150,7 +1166,11 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             const float rng = mx - mn;
             const float s = rng > 0.0f ? C::QMAX / rng : 1.0f;
             const float z0 = 0.0f - mn * s;      // +0 when min is a zero of either sign
-            const double sxs = addd_k<KB>(lane_sum_xs<WB>(xb, (double)s));
+            // with every weight of the tile below 1/2 (most tiles), x*s summed as s * sum x
+            const bool small = __ballot(fmaxf(-mn, mx) >= 0.5f) == 0;
+            double sxs;
+            if (small) sxs = (double)s * addd_k<KB>(lane_sum_x<WB>(xb));
+            else sxs = addd_k<KB>(lane_sum_xs<WB>(xb, (double)s));
             if (bleader) {
                 // The scale is fixed from here on: the tile's scales are stored now, one
                 // contiguous run per tile, rather than one by one as groups finish.
@@ -1287,7 +1307,10 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
     const float rng = mx - mn;
     const float s = rng > 0.0f ? C::QMAX / rng : 1.0f;
     const double sd = s;
-    const double X = addd_k<KB>(lane_sum_xs<WB>(xb, sd));
+    const bool small = __ballot(fmaxf(-mn, mx) >= 0.5f) == 0;   // as in the persistent INIT
+    double X;
+    if (small) X = sd * addd_k<KB>(lane_sum_x<WB>(xb));
+    else X = addd_k<KB>(lane_sum_xs<WB>(xb, sd));
     if (valid && bleader) gbl(J.scale)[gidx] = f2h(1.0f / s);
     // binary32 range test of the fast path: u of the extreme weights stays in range
     const float umn = mn, umx = mx;
