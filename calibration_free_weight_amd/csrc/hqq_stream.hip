@@ -197,7 +197,7 @@ __device__ __forceinline__ double bperm_d(int src, double v)
 }
 // Sum of a lane's E weights in binary64, for groups whose weights are all below 1/2 in
 // magnitude: each binary16 pair is added by v_dot2 against {1, 1}, exactly (a multiple of 2^-24
-// below 1 fits binary32; checked on every pattern class, subnormals included), and the pair
+// below 1 fits binary32; checked on the GPU for all 822,083,584 such pairs), and the pair
 // sums add exactly in binary64 (below 2^23 units of 2^-24). s * (this sum) then rounds the
 // exact sum x*s once, so it equals lane_sum_xs's result wherever that one is exact.
 template <int W>
