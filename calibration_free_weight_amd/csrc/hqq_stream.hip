@@ -203,12 +203,15 @@ __device__ __forceinline__ double bperm_d(int src, double v)
 template <int W>
 __device__ __forceinline__ double lane_sum_x(const uint32_t (&xb)[W])
 {
+    static_assert(W >= 4, "four partial sums");
     typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
     const hh2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    double acc[4];
 #pragma unroll
-    for (int i = 0; i < W; ++i)
-        acc[i & 3] += (double)__builtin_amdgcn_fdot2(__builtin_bit_cast(hh2, xb[i]), one, 0.0f, false);
+    for (int i = 0; i < W; ++i) {
+        const double p = (double)__builtin_amdgcn_fdot2(__builtin_bit_cast(hh2, xb[i]), one, 0.0f, false);
+        acc[i & 3] = i < 4 ? p : acc[i & 3] + p;
+    }
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 // LDS atomic swap of 8 bytes (ds_wrxchg_rtn_b64): stores v, returns the old contents.
@@ -379,12 +382,16 @@ struct Exact {
 
 // Exact (binary64) evaluation of one batch lane's EB weights (chunks c0.. of slot j) at zero
 // z. Rare: a rolled loop over the 16-byte chunks (one LDS read each), so it adds few
-// registers to the binary32 path; the binary64 sums are exact in any order.
-template <class C>
-__device__ __forceinline__ Exact eval_exact(const uint16_t *xs, int j, int c0, float s, float z)
+// registers to the binary32 path; the binary64 sums are exact in any order. CLAMP false when
+// no weight of the group can leave the code range at z or zb (the caller checks the extreme
+// weights), so rint(u) is the code; SB true adds the exact S at a second zero zb in the same
+// loop (returned in sb), sharing the loads and the conversions of the weights.
+template <class C, bool CLAMP, bool SB>
+__device__ __forceinline__ Exact eval_exact_t(const uint16_t *xs, int j, int c0, float s, float z,
+                                              float zb, double &sb)
 {
-    const double sd = s, zd = z, qm = C::QMAX;
-    double s_ = 0.0, q_ = 0.0, d_ = 0.0;
+    const double sd = s, zd = z, zbd = zb, qm = C::QMAX;
+    double s_ = 0.0, q_ = 0.0, d_ = 0.0, sb_ = 0.0;
 #pragma unroll 1
     for (int c = 0; c < C::EB / 8; ++c) {
         const u32x4 v = *reinterpret_cast<const u32x4 *>(xs + chunk_at<C::CS>(j, c0 + c));
@@ -392,14 +399,20 @@ __device__ __forceinline__ Exact eval_exact(const uint16_t *xs, int j, int c0, f
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint32_t h = i & 1 ? w4[i >> 1] >> 16 : w4[i >> 1] & 0xffffu;
-            const double u = fma((double)h2f(h), sd, zd);
-            const double c2 = fmin(fmax(rint(u), 0.0), qm);
+            const double x = h2f(h);
+            const double u = fma(x, sd, zd);
+            const double c2 = CLAMP ? fmin(fmax(rint(u), 0.0), qm) : rint(u);
             const double e = fabs(u - c2);
             s_ += e;
             q_ += c2;
             d_ = fmax(d_, e);
+            if constexpr (SB) {
+                const double ub = fma(x, sd, zbd);
+                sb_ += fabs(ub - (CLAMP ? fmin(fmax(rint(ub), 0.0), qm) : rint(ub)));
+            }
         }
     }
+    sb = sb_;
     return Exact{s_, q_, d_};
 }
 
@@ -998,13 +1011,30 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
                     const int c0 = sub * (EB / 8);
                     if (((fl >> 1) & 3) == kDecide) {
                         const float z = sa.z;
-                        const Exact xn = eval_exact<C>(xs, j, c0, s, z);
+                        // S at the accepted zero as well, where only its binary32 value is kept
+                        const bool need_sb = !(fl & kFirst) && !(fl & kSbExact);
+                        // u of the group's extreme weights (exact in binary64; u rises with x)
+                        // at both zeros: inside (-1/2, QMAX + 1/2), no code clamps
+                        const uint32_t mm = st_b[j].mnmx;
+                        const double sd = s, lo = h2f(mm & 0xffffu), hi = h2f(mm >> 16);
+                        const double ul = fmin(fma(lo, sd, (double)z), fma(lo, sd, (double)sa.zb));
+                        const double uh = fmax(fma(hi, sd, (double)z), fma(hi, sd, (double)sa.zb));
+                        const bool inr = ul > -0.5 && uh < C::QMAX + 0.5;
+                        const bool clamp_any = __ballot(!inr) != 0, sb_any = __ballot(need_sb) != 0;
+                        double sbx = 0.0;
+                        Exact xn;
+                        if (!clamp_any) {
+                            if (sb_any) xn = eval_exact_t<C, false, true>(xs, j, c0, s, z, sa.zb, sbx);
+                            else xn = eval_exact_t<C, false, false>(xs, j, c0, s, z, sa.zb, sbx);
+                        } else {
+                            if (sb_any) xn = eval_exact_t<C, true, true>(xs, j, c0, s, z, sa.zb, sbx);
+                            else xn = eval_exact_t<C, true, false>(xs, j, c0, s, z, sa.zb, sbx);
+                        }
                         const double S = addd_k<KB>(xn.S);
                         const float Q = (float)addd_k<KB>(xn.Q);
                         const float D = maxf_k<KB>((float)xn.D);
                         double Sb = st_c[j].Sb;
-                        if (!(fl & kFirst) && !(fl & kSbExact))
-                            Sb = addd_k<KB>(eval_exact<C>(xs, j, c0, s, sa.zb).S);
+                        if (need_sb) Sb = addd_k<KB>(sbx);
                         if ((fl & kFirst) || !a.early_stop || S <= Sb) {
                             if (bleader) {
                                 st_a[j].zb = z;
@@ -1192,7 +1222,7 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 }
 
 // Exact (binary64) evaluation of a lane's EB weights held in registers at zero z (the
-// lockstep kernel's form of eval_exact).
+// lockstep kernel's form of eval_exact_t).
 template <class C>
 __device__ __forceinline__ Exact eval_exact_regs(const uint32_t (&xb)[C::WB], float s, float z)
 {
