@@ -195,24 +195,47 @@ __device__ __forceinline__ double bperm_d(int src, double v)
     const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)(b >> 32));
     return __longlong_as_double((long long)((uint64_t)hi << 32 | lo));
 }
-// Sum of a lane's E weights in binary64, for groups whose weights are all below 1/2 in
-// magnitude: each binary16 pair is added by v_dot2 against {1, 1}, exactly (a multiple of 2^-24
-// below 1 fits binary32; checked on the GPU for all 822,083,584 such pairs), and the pair
-// sums add exactly in binary64 (below 2^23 units of 2^-24). s * (this sum) then rounds the
-// exact sum x*s once, so it equals lane_sum_xs's result wherever that one is exact.
-template <int W>
+// Sum of a lane's weights in binary64, for tiles whose weights all lie below 1/(2L) in
+// magnitude: v_dot2 against {1, 1} adds a binary16 pair and a running binary32 sum, and chains
+// of L pairs stay exact, since every partial sum is a multiple of 2^-24 below 1, which
+// binary32 holds (checked on the GPU: all 822,083,584 pairs below 1/2 with a zero addend, and
+// random chains of 2, 4 and 8 pairs, subnormals included). The chain sums add exactly in
+// binary64 (below 2^23 units of 2^-24). s * (this sum) then rounds the exact sum x*s once, so
+// it equals lane_sum_xs's result wherever that one is exact.
+template <int W, int L>
 __device__ __forceinline__ double lane_sum_x(const uint32_t (&xb)[W])
 {
-    static_assert(W >= 4, "four partial sums");
+    static_assert(W % L == 0, "whole chains");
+    constexpr int NC = W / L, NA = NC < 4 ? NC : 4;
     typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
     const hh2 one = {(_Float16)1.0f, (_Float16)1.0f};
-    double acc[4];
+    double acc[NA];
 #pragma unroll
-    for (int i = 0; i < W; ++i) {
-        const double p = (double)__builtin_amdgcn_fdot2(__builtin_bit_cast(hh2, xb[i]), one, 0.0f, false);
-        acc[i & 3] = i < 4 ? p : acc[i & 3] + p;
+    for (int c = 0; c < NC; ++c) {
+        float p = __builtin_amdgcn_fdot2(__builtin_bit_cast(hh2, xb[c * L]), one, 0.0f, false);
+#pragma unroll
+        for (int l = 1; l < L; ++l)
+            p = __builtin_amdgcn_fdot2(__builtin_bit_cast(hh2, xb[c * L + l]), one, p, false);
+        acc[c % NA] = c < NA ? (double)p : acc[c % NA] + (double)p;
     }
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if constexpr (NA == 4) return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    else if constexpr (NA == 2) return acc[0] + acc[1];
+    else return acc[0];
+}
+// A lane's binary64 sum of x for a tile whose largest magnitude am (wave-uniform choice) is
+// below 1/2, with the longest exact chains am allows.
+template <int W>
+__device__ __forceinline__ double lane_sum_x_tile(const uint32_t (&xb)[W], float am)
+{
+    if (__ballot(am >= 0.25f)) return lane_sum_x<W, 1>(xb);
+    if constexpr (W % 4 == 0) {
+        if (__ballot(am >= 0.125f)) return lane_sum_x<W, 2>(xb);
+        return lane_sum_x<W, 4>(xb);
+    } else if constexpr (W % 2 == 0) {
+        return lane_sum_x<W, 2>(xb);
+    } else {
+        return lane_sum_x<W, 1>(xb);
+    }
 }
 // LDS atomic swap of 8 bytes (ds_wrxchg_rtn_b64): stores v, returns the old contents.
 __device__ __forceinline__ uint64_t xchg_l(uint64_t *p, uint64_t v)
@@ -1197,10 +1220,10 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
             const float s = rng > 0.0f ? C::QMAX / rng : 1.0f;
             const float z0 = 0.0f - mn * s;      // +0 when min is a zero of either sign
             // with every weight of the tile below 1/2 (most tiles), x*s summed as s * sum x
-            const bool small = __ballot(fmaxf(-mn, mx) >= 0.5f) == 0;
+            const float am = fmaxf(-mn, mx);
             double sxs;
-            if (small) sxs = (double)s * addd_k<KB>(lane_sum_x<WB>(xb));
-            else sxs = addd_k<KB>(lane_sum_xs<WB>(xb, (double)s));
+            if (__ballot(am >= 0.5f)) sxs = addd_k<KB>(lane_sum_xs<WB>(xb, (double)s));
+            else sxs = (double)s * addd_k<KB>(lane_sum_x_tile<WB>(xb, am));
             if (bleader) {
                 // The scale is fixed from here on: the tile's scales are stored now, one
                 // contiguous run per tile, rather than one by one as groups finish.
@@ -1337,10 +1360,10 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
     const float rng = mx - mn;
     const float s = rng > 0.0f ? C::QMAX / rng : 1.0f;
     const double sd = s;
-    const bool small = __ballot(fmaxf(-mn, mx) >= 0.5f) == 0;   // as in the persistent INIT
+    const float am = fmaxf(-mn, mx);                               // as in the persistent INIT
     double X;
-    if (small) X = sd * addd_k<KB>(lane_sum_x<WB>(xb));
-    else X = addd_k<KB>(lane_sum_xs<WB>(xb, sd));
+    if (__ballot(am >= 0.5f)) X = addd_k<KB>(lane_sum_xs<WB>(xb, sd));
+    else X = sd * addd_k<KB>(lane_sum_x_tile<WB>(xb, am));
     if (valid && bleader) gbl(J.scale)[gidx] = f2h(1.0f / s);
     // binary32 range test of the fast path: u of the extreme weights stays in range
     const float umn = mn, umx = mx;

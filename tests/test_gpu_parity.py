@@ -118,6 +118,41 @@ def test_edge_inputs(O, dev):
             compare(O, W, out, nbits, g, 16, label=name)
 
 
+def magnitude_band_weights(rows, cols, seed, amax):
+    """Synthetic weights scaled so that the largest magnitude is amax, with 1 % of the
+    entries replaced by binary16 subnormals of either sign: every tile then takes the same
+    branch of the solver's binary64 sum of x*s (chains of 4, 2 or 1 exact pair sums below
+    1/8, 1/4 and 1/2; products one by one from 1/2 up)."""
+    gen = torch.Generator().manual_seed(seed)
+    W = synth.student_t_weights(rows, cols, seed).float()
+    W = (W * (amax / W.abs().max())).half()
+    n = W.numel()
+    idx = torch.randperm(n, generator=gen)[: n // 100]
+    k = torch.randint(1, 1024, (idx.numel(),), generator=gen)
+    sign = torch.where(torch.rand(idx.numel(), generator=gen) < 0.5, 0x8000, 0)
+    flat = W.reshape(-1).view(torch.int16)
+    flat[idx] = (k | sign).to(torch.int16)
+    assert float(W.abs().max()) <= amax * (1 + 2.0 ** -10)
+    return W
+
+
+@pytest.mark.parametrize("amax", [3.0, 0.45, 0.2, 0.1, 2.0 ** -14])
+@pytest.mark.parametrize("layout", [1, 3], ids=["persistent", "lockstep"])
+def test_weight_magnitude_bands(O, dev, layout, amax):
+    """Each branch of the binary64 sum of x*s at the min-max start (by the tile's largest
+    magnitude), in both solver kernels, bit-exact against the oracle."""
+    try:
+        hqq.hqq_debug_solver(pass_layout=layout)
+        for g in (16, 64, 128):
+            for zero_bits in (16, 8):
+                print(f"layout {layout} amax {amax} g={g} zero={zero_bits}", flush=True)
+                W = magnitude_band_weights(32, g * 24, 700 + g, amax).to(dev)
+                out = run(W, 4, g, zero_bits)
+                compare(O, W, out, 4, g, zero_bits, label=f"layout {layout} amax {amax} g{g}")
+    finally:
+        hqq.hqq_debug_solver()
+
+
 def half_grid_groups(rows, cols, g, nbits, seed, frac=1.0):
     """Groups whose first evaluation lands exactly on rounding boundaries: each group holds
     its min 0, its max qmax/16 and otherwise values (k + 1/2)/16, so s = 16, z0 = 0 and
