@@ -47,6 +47,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "hqq_internal.h"
 
@@ -1315,7 +1316,8 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
     using C = Cfg<NBITS, G>;
     constexpr int EB = C::EB, KB = C::KB, GB = C::GB, WB = C::WB;
     __shared__ __attribute__((aligned(4))) uint8_t stage[NBITS == 3 ? 64 * EB : 4];
-    __shared__ __attribute__((aligned(16))) uint32_t xl[64 * WB];   // the wave's weights (exact turns)
+    __shared__ __attribute__((aligned(16))) uint32_t xl[64 * WB];   // the wave's weights, lane-major
+    __shared__ int lead_of[64];                                      // spread rounds: slot -> leader
     const int lane = threadIdx.x;
     const int k = lane / KB, sub = lane % KB;
     const bool bleader = sub == 0;
@@ -1345,6 +1347,14 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
             xb[4 * i + 3] = v.w;
         }
     }
+    // An LDS copy of the weights for the turns that spread groups over the whole wave (the
+    // weights never change, so it is written once): group g of the tile, led by lane L = g*KB,
+    // holds words L*WB .. L*WB + G/2 - 1 in element order.
+#pragma unroll
+    for (int i = 0; i < WB / 4; ++i)
+        *reinterpret_cast<u32x4 *>(xl + lane * WB + 4 * i) =
+            u32x4{xb[4 * i], xb[4 * i + 1], xb[4 * i + 2], xb[4 * i + 3]};
+    __syncthreads();
     // Dead zone of the shrink (as in the persistent kernel).
     const double tau_exp = -1.0 / (2.0 - (double)a.p);
     float beta_last = a.beta0;
@@ -1402,7 +1412,62 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
         }
     };
 
-    while (__ballot(step != kStepDone)) {
+    // Binary32 evaluation of the groups in the fast step, spread over the whole wave when
+    // few of them are left (mf: their leader lanes, nf of them): WPL = 4*R weights per lane,
+    // read from the LDS copy four at a time, and LPG = G/WPL lanes per group; the q-th group
+    // takes lanes q*LPG .. q*LPG+LPG-1. R and LPG are wave-uniform run-time values, so one
+    // code path serves every width. Every lane of such a group receives its S, T and D. The
+    // sums add in another order than eval_fast's, in chains no longer than its, so the margins
+    // below cover them alike; D is a maximum and Q depends on T only through rne, far from a
+    // half, so both come out the same.
+    auto spread_eval = [&](uint64_t mf, int nf, int R, int lg, float &S, float &T, float &D) {
+        const int LPG = 1 << lg;
+        const int slot = lane >> lg, part = lane & (LPG - 1);
+        if ((mf >> lane) & 1ull) lead_of[__builtin_popcountll(mf & ((1ull << lane) - 1ull))] = lane;
+        __syncthreads();
+        const int lead = slot < nf ? lead_of[slot] : 0;   // idle slots evaluate lane 0's group
+        const float sv = bperm_f(lead, s), zv = bperm_f(lead, z);
+        const uint32_t *src = xl + lead * WB + part * 2 * R;
+        float sp = 0.0f, tp = 0.0f, dp = 0.0f;
+#pragma unroll 1
+        for (int r = 0; r < R; ++r) {
+            const u32x2 v = *reinterpret_cast<const u32x2 *>(src + 2 * r);
+            const uint32_t xr[2] = {v.x, v.y};
+            float sr, tr, dr;
+            eval_fast<NBITS, 2>(xr, sv, zv, sr, tr, dr);
+            sp += sr;
+            tp += tr;
+            dp = fmaxf(dp, dr);
+        }
+        // butterflies within the LPG lanes of a slot (uniform branches)
+        if (lg >= 1) { sp += dppf<0xb1>(sp); tp += dppf<0xb1>(tp); dp = fmaxf(dp, dppf<0xb1>(dp)); }
+        if (lg >= 2) { sp += dppf<0x4e>(sp); tp += dppf<0x4e>(tp); dp = fmaxf(dp, dppf<0x4e>(dp)); }
+        if (lg >= 3) { sp += dppf<0x141>(sp); tp += dppf<0x141>(tp); dp = fmaxf(dp, dppf<0x141>(dp)); }
+        if (lg >= 4) { sp += dppf<0x140>(sp); tp += dppf<0x140>(tp); dp = fmaxf(dp, dppf<0x140>(dp)); }
+        if (lg >= 5) {
+            sp += __shfl_xor(sp, 16);
+            tp += __shfl_xor(tp, 16);
+            dp = fmaxf(dp, __shfl_xor(dp, 16));
+        }
+        if (lg >= 6) {
+            sp += __shfl_xor(sp, 32);
+            tp += __shfl_xor(tp, 32);
+            dp = fmaxf(dp, __shfl_xor(dp, 32));
+        }
+        const int src_lane = __builtin_popcountll(mf & ((1ull << (lane - sub)) - 1ull)) << lg;
+        S = bperm_f(src_lane, sp);
+        T = bperm_f(src_lane, tp);
+        D = bperm_f(src_lane, dp);
+    };
+
+    for (;;) {
+        // The weights pass an empty asm at the top of every turn, so their binary32 forms are
+        // not loop-invariant: the evaluation converts on the fly (v_fma_mix) rather than the
+        // compiler holding all EB converted weights across the loop (32 more registers, one
+        // wave fewer per SIMD at EB = 32).
+#pragma unroll
+        for (int i = 0; i < WB; ++i) asm volatile("" : "+v"(xb[i]));
+        if (!__ballot(step != kStepDone)) break;
         if (--budget <= 0) {
             ran_out = true;
             break;
@@ -1413,13 +1478,33 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
             step = clamp ? (uint8_t)kStepExact : step;           // may clamp
         }
         // ---- binary32 evaluation; the decision as in the persistent kernel, with selects ----
+        // A turn with few groups in the fast step spreads them over the wave (4, 8 or 16
+        // weights per lane instead of EB); otherwise each group's own lanes evaluate it.
+        float S = 0.0f, T = 0.0f, D = 0.0f;
+        bool spread = false;
+        {
+            const uint64_t mf = __ballot(step == kStepFast && bleader);
+            const int nf = __builtin_popcountll(mf);
+            // the fewest weights per lane (4, 8 or 16, fewer than EB) that fit nf groups
+            int R = 0;
+            if (nf > 0 && EB > 4 && nf * G <= 64 * 4) R = 1;
+            else if (nf > 0 && EB > 8 && nf * G <= 64 * 8) R = 2;
+            else if (nf > 0 && EB > 16 && nf * G <= 64 * 16) R = 4;
+            if (R > 0) {
+                // lanes per group: G / (4 R), a power of two
+                const int lg = __builtin_ctz((unsigned)G) - 2 - __builtin_ctz((unsigned)R);
+                spread_eval(mf, nf, R, lg, S, T, D);
+                spread = true;
+            }
+        }
         if (step == kStepFast) {
-            float S, T, D;
-            eval_fast<NBITS, WB>(xb, s, z, S, T, D);
-            if (KB > 1) {
-                S = addf_k<KB>(S);
-                T = addf_k<KB>(T);
-                D = maxf_k<KB>(D);
+            if (!spread) {
+                eval_fast<NBITS, WB>(xb, s, z, S, T, D);
+                if (KB > 1) {
+                    S = addf_k<KB>(S);
+                    T = addf_k<KB>(T);
+                    D = maxf_k<KB>(D);
+                }
             }
             const float Q = (float)rint(fma((double)G, (double)z, X) - (double)T);
             const float Sb32 = (float)Sb;
@@ -1478,11 +1563,6 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
             // four weights per lane instead of EB.
             constexpr int LPG = G / 4, NPC = 64 / LPG;
             const bool any_sbx = __ballot(step == kStepExact && !first && !sbexact) != 0;
-#pragma unroll
-            for (int i = 0; i < WB / 4; ++i)
-                *reinterpret_cast<u32x4 *>(xl + lane * WB + 4 * i) =
-                    u32x4{xb[4 * i], xb[4 * i + 1], xb[4 * i + 2], xb[4 * i + 3]};
-            __syncthreads();
             const int slot = lane / LPG, part = lane % LPG;
             uint64_t m_left = __ballot(step == kStepExact && bleader);
             while (m_left) {
