@@ -43,7 +43,12 @@ __device__ __forceinline__ float unkey(uint32_t k)
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// A block takes kFinishRounds rounds of 256 x kFinishPerThread items; in a round a thread
+// takes kFinishPerThread items 256 apart and issues all their loads before any store, so
+// the memory latency is paid once per round rather than once per item.
 constexpr int kFinishPerThread = 8;
+constexpr int kFinishRounds = 2;
+constexpr int64_t kFinishPerBlock = 256 * kFinishPerThread * kFinishRounds;
 
 // One job's view for the finish kernel, held in registers: the kernel's stores cannot then
 // force the job descriptor to be reloaded for every item.
@@ -83,20 +88,65 @@ __device__ __forceinline__ FinishJob finish_job(const DevJob &J, int64_t end, ui
     return f;
 }
 
+// The 8-bit code of a zero on the tensor's grid.
+__device__ __forceinline__ uint8_t zero_code(const FinishJob &f, float z)
+{
+    const float v = rintf((z - f.basef) / f.step);
+    return (uint8_t)fminf(fmaxf(v, 0.0f), 255.0f);
+}
+
+// Group i's 3-bit code stream starts inside a 10-code word that group i - 1 ends in.
+__device__ __forceinline__ bool shares_word(const FinishJob &f, uint32_t i)
+{
+    return i >= 1 && ((i % 10u) * (f.g % 10u)) % 10u != 0;
+}
+
 __device__ __forceinline__ void finish_item(const FinishJob &f, int64_t item)
 {
     const uint32_t i = (uint32_t)(item - f.item0);  // a group index (< 2^32 per tensor)
     if (f.zq) {
-        const float v = rintf((f.zero32[i] - f.basef) / f.step);
-        f.zq[i] = (uint8_t)fminf(fmaxf(v, 0.0f), 255.0f);
+        f.zq[i] = zero_code(f, f.zero32[i]);
         if (i == 0) {
             f.meta[0] = f.h_step;
             f.meta[1] = f.h_base;
         }
     }
-    if (f.stash && i >= 1 && ((i % 10u) * (f.g % 10u)) % 10u != 0) {
+    if (f.stash && shares_word(f, i)) {
         const int64_t w = (int64_t)i * f.g / 10;
         f.packed[w] = f.stash[i - 1].x | f.stash[i].y;
+    }
+}
+
+// One round of kFinishPerThread items that all belong to job f: every load first, then the
+// codes and the joined words.
+__device__ __forceinline__ void finish_round(const FinishJob &f, int64_t item)
+{
+    constexpr int P = kFinishPerThread;
+    uint32_t i[P];
+#pragma unroll
+    for (int k = 0; k < P; ++k) i[k] = (uint32_t)(item + 256 * k - f.item0);
+    if (f.zq) {
+        float z[P];
+#pragma unroll
+        for (int k = 0; k < P; ++k) z[k] = __builtin_nontemporal_load(f.zero32 + i[k]);
+#pragma unroll
+        for (int k = 0; k < P; ++k) f.zq[i[k]] = zero_code(f, z[k]);
+        if (i[0] == 0) {
+            f.meta[0] = f.h_step;
+            f.meta[1] = f.h_base;
+        }
+    }
+    if (f.stash) {
+        uint32_t word[P];
+        bool join[P];
+#pragma unroll
+        for (int k = 0; k < P; ++k) {
+            join[k] = shares_word(f, i[k]);
+            word[k] = join[k] ? f.stash[i[k] - 1].x | f.stash[i[k]].y : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < P; ++k)
+            if (join[k]) f.packed[(int64_t)i[k] * f.g / 10] = word[k];
     }
 }
 
@@ -105,57 +155,64 @@ __global__ void __launch_bounds__(256) finish_kernel(const DevJob *table, int n_
 {
     __shared__ int job_sh;
     __shared__ uint32_t grid_sh[2];                 // job_sh's (min, max) keys, reduced
-    const int64_t base = (int64_t)blockIdx.x * 256 * kFinishPerThread;
-    if (threadIdx.x == 0) {
-        int lo = 0, hi = n_jobs - 1;                // last job with item0 <= base
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) / 2;
-            if (table[mid].item0 <= base) lo = mid;
-            else hi = mid - 1;
-        }
-        job_sh = lo;
-    }
-    __syncthreads();
-    const int j0 = job_sh;
-    // The first wave reduces the first job's key copies once for the block (one per lane).
+    const int64_t base = (int64_t)blockIdx.x * kFinishPerBlock;
     if (threadIdx.x < 64) {
+        // The last job with item0 <= base: the first wave tests 64 jobs per step, with
+        // independent loads (item0 rises with the job index).
+        int last = 0;
+        for (int j0 = 0; j0 < n_jobs; j0 += 64) {
+            const int j = j0 + (int)threadIdx.x;
+            const uint64_t m = __ballot(j < n_jobs && table[j].item0 <= base);
+            if (m == 0) break;
+            last = j0 + 63 - __builtin_clzll(m);
+            if (m != ~0ull) break;
+        }
+        // The first wave then reduces that job's key copies once for the block (one per lane).
         uint32_t kmin = 0xffffffffu, kmax = 0u;
-        if (table[j0].zq && threadIdx.x < kMinmaxSlots) {
-            kmin = table[j0].minmax[kMinmaxStride * threadIdx.x];
-            kmax = table[j0].minmax[kMinmaxStride * threadIdx.x + 1];
+        if (table[last].zq && threadIdx.x < kMinmaxSlots) {
+            kmin = table[last].minmax[kMinmaxStride * threadIdx.x];
+            kmax = table[last].minmax[kMinmaxStride * threadIdx.x + 1];
         }
         for (int d = 32; d >= 1; d >>= 1) {
             kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
             kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
         }
         if (threadIdx.x == 0) {
+            job_sh = last;
             grid_sh[0] = kmin;
             grid_sh[1] = kmax;
         }
     }
     __syncthreads();
+    const int j0 = job_sh;
     const FinishJob f0 =
         finish_job(table[j0], j0 + 1 < n_jobs ? table[j0 + 1].item0 : n_items, grid_sh[0], grid_sh[1]);
     int j = j0;
-    for (int r = 0; r < kFinishPerThread; ++r) {
-        const int64_t item = base + (int64_t)r * 256 + threadIdx.x;
-        if (item >= n_items) break;
-        if (item < f0.end) {
-            finish_item(f0, item);
+    for (int r = 0; r < kFinishRounds; ++r) {
+        const int64_t rbase = base + (int64_t)r * 256 * kFinishPerThread;
+        if (rbase + 256 * kFinishPerThread <= f0.end) {   // the whole round in the first job
+            finish_round(f0, rbase + threadIdx.x);
             continue;
         }
-        // a later job in this block (a block spans 2,048 items, a tensor far more): its
-        // descriptor and key copies straight from memory
-        while (j + 1 < n_jobs && table[j + 1].item0 <= item) ++j;
-        uint32_t kmin = 0xffffffffu, kmax = 0u;
-        if (table[j].zq)
-            for (int p = 0; p < kMinmaxSlots; ++p) {
-                kmin = min(kmin, table[j].minmax[kMinmaxStride * p]);
-                kmax = max(kmax, table[j].minmax[kMinmaxStride * p + 1]);
+        for (int k = 0; k < kFinishPerThread; ++k) {
+            const int64_t item = rbase + (int64_t)k * 256 + threadIdx.x;
+            if (item >= n_items) break;
+            if (item < f0.end) {
+                finish_item(f0, item);
+                continue;
             }
-        const FinishJob fj =
-            finish_job(table[j], j + 1 < n_jobs ? table[j + 1].item0 : n_items, kmin, kmax);
-        finish_item(fj, item);
+            // a later job in this block: its descriptor and key copies straight from memory
+            while (j + 1 < n_jobs && table[j + 1].item0 <= item) ++j;
+            uint32_t kmin = 0xffffffffu, kmax = 0u;
+            if (table[j].zq)
+                for (int p = 0; p < kMinmaxSlots; ++p) {
+                    kmin = min(kmin, table[j].minmax[kMinmaxStride * p]);
+                    kmax = max(kmax, table[j].minmax[kMinmaxStride * p + 1]);
+                }
+            const FinishJob fj =
+                finish_job(table[j], j + 1 < n_jobs ? table[j + 1].item0 : n_items, kmin, kmax);
+            finish_item(fj, item);
+        }
     }
 }
 
@@ -622,8 +679,7 @@ unsigned grid_for(int64_t items, int per_block)
 hipError_t launch_finish(const DevJob *table, int n_jobs, int64_t n_items, hipStream_t stream)
 {
     if (n_items == 0 || n_jobs == 0) return hipSuccess;
-    const int64_t per_block = 256 * kFinishPerThread;
-    const int64_t blocks = (n_items + per_block - 1) / per_block;
+    const int64_t blocks = (n_items + kFinishPerBlock - 1) / kFinishPerBlock;
     hipLaunchKernelGGL(finish_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, table, n_jobs,
                        n_items);
     return hipGetLastError();
