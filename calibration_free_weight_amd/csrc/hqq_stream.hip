@@ -1247,15 +1247,15 @@ stream_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 
 // Exact (binary64) evaluation of a lane's EB weights held in registers at zero z (the
 // lockstep kernel's form of eval_exact_t).
-template <class C>
-__device__ __forceinline__ Exact eval_exact_regs(const uint32_t (&xb)[C::WB], float s, float z)
+template <class C, int WB>
+__device__ __forceinline__ Exact eval_exact_regs(const uint32_t (&xb)[WB], float s, float z)
 {
     const double sd = s, zd = z, qm = C::QMAX;
     double s_ = 0.0, q_ = 0.0, d_ = 0.0;
     // two words (four weights) per turn: a register array indexed in a rolled loop costs an
     // indexed move per index, and the binary64 sums are exact in any order
 #pragma unroll 1
-    for (int w = 0; w < C::WB; w += 2) {
+    for (int w = 0; w < WB; w += 2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t v = xb[w + (i >> 1)];
@@ -1273,14 +1273,14 @@ __device__ __forceinline__ Exact eval_exact_regs(const uint32_t (&xb)[C::WB], fl
 
 // eval_exact_regs at z, and in the same loop the exact error sum at a second zero zb (each
 // sum in the same order as eval_exact_regs would take it).
-template <class C>
-__device__ __forceinline__ Exact eval_exact2_regs(const uint32_t (&xb)[C::WB], float s, float z,
+template <class C, int WB>
+__device__ __forceinline__ Exact eval_exact2_regs(const uint32_t (&xb)[WB], float s, float z,
                                                   float zb, double &Sb_out)
 {
     const double sd = s, zd = z, zbd = zb, qm = C::QMAX;
     double s_ = 0.0, q_ = 0.0, d_ = 0.0, sb_ = 0.0;
 #pragma unroll 1
-    for (int w = 0; w < C::WB; w += 2) {
+    for (int w = 0; w < WB; w += 2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t v = xb[w + (i >> 1)];
@@ -1310,11 +1310,13 @@ __device__ __forceinline__ Exact eval_exact2_regs(const uint32_t (&xb)[C::WB], f
 // Every decision is the persistent kernel's, so the results are identical.
 enum : uint8_t { kStepFast = 0, kStepExact = 1, kStepShrink = 2, kStepDone = 3 };
 
-template <int NBITS, int G>
+template <int NBITS, int G, int EBL>
 __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob *__restrict__ jobs)
 {
     using C = Cfg<NBITS, G>;
-    constexpr int EB = C::EB, KB = C::KB, GB = C::GB, WB = C::WB;
+    // EBL weights per lane: the batch layout's EB, or more (fewer lanes per group, more groups
+    // per tile) for a class of one tensor, whose tiles need not line up with the plan's
+    constexpr int EB = EBL, KB = G / EB, GB = 64 / KB, WB = EB / 2;
     __shared__ __attribute__((aligned(4))) uint8_t stage[NBITS == 3 ? 64 * EB : 4];
     __shared__ __attribute__((aligned(16))) uint32_t xl[64 * WB];   // the wave's weights, lane-major
     __shared__ int lead_of[64];                                      // spread rounds: slot -> leader
@@ -1478,18 +1480,19 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
             step = clamp ? (uint8_t)kStepExact : step;           // may clamp
         }
         // ---- binary32 evaluation; the decision as in the persistent kernel, with selects ----
-        // A turn with few groups in the fast step spreads them over the wave (4, 8 or 16
-        // weights per lane instead of EB); otherwise each group's own lanes evaluate it.
+        // A turn with few groups in the fast step spreads them over the wave (4 to 32
+        // weights per lane, fewer than EB); otherwise each group's own lanes evaluate it.
         float S = 0.0f, T = 0.0f, D = 0.0f;
         bool spread = false;
         {
             const uint64_t mf = __ballot(step == kStepFast && bleader);
             const int nf = __builtin_popcountll(mf);
-            // the fewest weights per lane (4, 8 or 16, fewer than EB) that fit nf groups
+            // the fewest weights per lane (4, 8, 16 or 32, fewer than EB) that fit nf groups
             int R = 0;
             if (nf > 0 && EB > 4 && nf * G <= 64 * 4) R = 1;
             else if (nf > 0 && EB > 8 && nf * G <= 64 * 8) R = 2;
             else if (nf > 0 && EB > 16 && nf * G <= 64 * 16) R = 4;
+            else if (nf > 0 && EB > 32 && nf * G <= 64 * 32) R = 8;
             if (R > 0) {
                 // lanes per group: G / (4 R), a power of two
                 const int lg = __builtin_ctz((unsigned)G) - 2 - __builtin_ctz((unsigned)R);
@@ -1542,22 +1545,23 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
         }
         // ---- exact decision (binary64), for the groups the fast path could not settle; the
         //      accepted error is re-evaluated exactly (at zb) when the fast path accepted it.
-        //      A group held by one lane (g16, g32) sums its errors element by element, in the
-        //      oracle's order, which fixes the result even where a sum rounds.
-        if (KB == 1 && __ballot(step == kStepExact)) {
+        //      Groups of 16 and 32 weights (one lane each) sum their errors element by
+        //      element, in the oracle's order, which fixes the result even where a sum rounds.
+        if (G < 64 && __ballot(step == kStepExact)) {
             const bool any_sbx = __ballot(step == kStepExact && !first && !sbexact) != 0;
             if (step == kStepExact) {
                 double sbx_l = 0.0;
-                const Exact xn = any_sbx ? eval_exact2_regs<C>(xb, s, z, zb, sbx_l)
-                                         : eval_exact_regs<C>(xb, s, z);
+                const Exact xn = any_sbx ? eval_exact2_regs<C, WB>(xb, s, z, zb, sbx_l)
+                                         : eval_exact_regs<C, WB>(xb, s, z);
                 double Sbx = Sb;
                 if (!first && !sbexact) Sbx = sbx_l;
                 exact_decide(xn.S, (float)xn.Q, (float)xn.D, Sbx);
             }
-        } else if (KB > 1 && __ballot(step == kStepExact)) {
-            // A group spread over several lanes already sums in another order than the
-            // oracle's, relying on the sums being exact (they are unless a group's range is
-            // extreme, the oracle's own precision reading). A turn has few such groups, so
+        } else if (G >= 64 && __ballot(step == kStepExact)) {
+            // Groups of 64 or more weights already sum in another order than the oracle's
+            // in their binary32 turns (over several lanes in the plan's layout), relying on
+            // the sums being exact (they are unless a group's range is extreme, the oracle's
+            // own precision reading). A turn has few such groups, so
             // their weights are spread over the whole wave first (through LDS; LPG lanes of
             // four weights per group, NPC groups per round): the binary64 loop then takes
             // four weights per lane instead of EB.
@@ -1745,18 +1749,34 @@ __global__ void __launch_bounds__(64) lockstep_kernel(StreamArgs a, const DevJob
         __hip_atomic_fetch_or(gbl(a.status), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int NBITS, int G, int EBL>
+hipError_t launch_lockstep_eb(StreamArgs a, hipStream_t stream)
+{
+    constexpr int GB = 64 / (G / EBL);
+    const int64_t fixed = step_budget();
+    // every loop turn advances at least one group by one step; a group takes at most
+    // 2*(iters + 1) evaluations and updates plus its exact decisions
+    a.budget0 = fixed > 0 ? fixed : 8 * (int64_t)(a.iters + 4) * GB;
+    a.budget_tile = 0;
+    hipLaunchKernelGGL((lockstep_kernel<NBITS, G, EBL>), dim3((unsigned)a.n_tiles), dim3(64), 0,
+                       stream, a, a.jobs);
+    return hipGetLastError();
+}
+
 template <int NBITS, int G>
 hipError_t launch_lockstep(StreamArgs a, hipStream_t stream)
 {
     using C = Cfg<NBITS, G>;
-    const int64_t fixed = step_budget();
-    // every loop turn advances at least one group by one step; a group takes at most
-    // 2*(iters + 1) evaluations and updates plus its exact decisions
-    a.budget0 = fixed > 0 ? fixed : 8 * (int64_t)(a.iters + 4) * C::GB;
-    a.budget_tile = 0;
-    hipLaunchKernelGGL((lockstep_kernel<NBITS, G>), dim3((unsigned)a.n_tiles), dim3(64), 0,
-                       stream, a, a.jobs);
-    return hipGetLastError();
+    // A class of one tensor at g64 runs one lane per group (GB2 = 64 groups per tile, twice
+    // the plan's GB): each turn's decision then serves twice the groups, and the registers
+    // still allow four waves per SIMD (at g128 and g256 they would not). Its last tile still
+    // starts inside the tensor, since the plan's last tile holds a group.
+    constexpr int EB2 = G == 64 ? 64 : C::EB, GB2 = 64 / (G / EB2);
+    if (EB2 != C::EB && a.n_jobs == 1) {
+        a.n_tiles = (a.n_tiles * C::GB + GB2 - 1) / GB2;
+        return launch_lockstep_eb<NBITS, G, EB2>(a, stream);
+    }
+    return launch_lockstep_eb<NBITS, G, C::EB>(a, stream);
 }
 
 template <int NBITS, int G, int EPL>
